@@ -1,0 +1,77 @@
+"""Planted mistakes: each test compiles a copy of the oracle with one plausible
+error (a dropped term, a wrong index or divisor, a flipped tie rule, a missing
+mask) and checks that at least one of the oracle's pins now fails.  This shows
+the pins constrain the oracle; the mistakes live only in temporary copies,
+on the CPU.
+"""
+import contextlib
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+
+import test_oracle_attention as T_att
+import test_oracle_gate_select as T_gs
+import test_oracle_pipeline as T_pipe
+
+
+@contextlib.contextmanager
+def mutated_oracle(tmp_path, old: str, new: str, count: int = 1):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == count, f"mutation anchor occurs {src.count(old)} times: {old!r}"
+    (tmp_path / "seer_oracle.c").write_text(src.replace(old, new))
+    shutil.copy(os.path.join(oracle._HERE, "seer_oracle.h"), tmp_path / "seer_oracle.h")
+    lib_path = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-std=c11", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", lib_path,
+                    str(tmp_path / "seer_oracle.c"), "-lm"], check=True, capture_output=True)
+    saved = oracle._load()
+    oracle._lib = oracle._bind(lib_path)
+    try:
+        yield
+    finally:
+        oracle._lib = saved
+
+
+def fails(*checks) -> bool:
+    """True if at least one pin check raises (assertion or numeric mismatch)."""
+    for fn in checks:
+        try:
+            fn()
+        except (AssertionError, ValueError):
+            return True
+    return False
+
+
+MUTATIONS = [
+    ("tail not attended", "        in_t[t] = 1;\n\n    /* D6", "        (void)t;\n\n    /* D6",
+     lambda: T_att.test_all_blocks_selected_equals_dense_attention(4, 64, 300, 64)),
+    ("softmax scale dropped", "z[t] = scale * dot;", "z[t] = dot;",
+     lambda: T_att.test_all_blocks_selected_equals_dense_attention(4, 64, 300, 64)),
+    ("tie toward the higher index", "(S[ids[b]] > S[ids[a]])", "(S[ids[b]] >= S[ids[a]])",
+     T_gs.test_selection_ties_go_to_lower_index_and_output_ascends),
+    ("transposed query projection", "wq[(int64_t)r * d + e]", "wq[(int64_t)e * dg + r]",
+     T_gs.test_gate_single_entry_projections_closed_form),
+    ("pooling divisor off by one", "kpool[(int64_t)j * d + c] = sum / bs;",
+     "kpool[(int64_t)j * d + c] = sum / (bs - 1);", T_gs.test_pool_constant_block_is_that_row),
+    ("group sum instead of mean", "S[j] = mean / G;", "S[j] = mean;",
+     T_gs.test_gate_identity_projections_score_group_mean_query),
+    ("pooled block offset wrong", "for (int t = j * bs; t < (j + 1) * bs; ++t)\n                sum +=",
+     "for (int t = j * bs + 1; t < (j + 1) * bs + 1; ++t)\n                sum +=",
+     T_gs.test_pool_ramp_closed_form),
+    ("keep count floors", "* keep_num + keep_den - 1) / keep_den;", "* keep_num) / keep_den + 1;",
+     T_pipe.test_prefill_keep_counts_golden),
+    ("prefill causal mask dropped", "for (int tt = 0; tt <= t; ++tt)", "for (int tt = 0; tt < L; ++tt)",
+     lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
+]
+
+
+@pytest.mark.parametrize("name,old,new,check", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, check):
+    count = open(oracle._SRC).read().count(old)
+    with mutated_oracle(tmp_path, old, new, count=count):
+        assert fails(check), f"no pin caught: {name}"
+    # and the unmodified oracle passes the same check
+    check()
