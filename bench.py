@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of one gated sparse decode step on one MI355X.
+
+A step is one pass of the decode hot path for one attention layer of a batch:
+pooled-key update for blocks completed at this token (only when a block
+completes), gate scores, token-budget block selection, and split-KV sparse
+decode with its log-sum-exp merge.  Default workload: batch 16, 32 query /
+8 KV heads, head_dim 128, context 65536, 128-token blocks, budget 6553 tokens
+-> 51 of 512 blocks kept (90% sparsity), keys of 5% of the blocks mean-shifted.
+
+Several layers' caches are rotated so that consecutive steps read different
+memory (as the layers of a model do); with inputs resident in HBM, the value
+is effective KV bandwidth: bytes of the kept K/V blocks (plus tail, query,
+output and ids) per step divided by the measured step time.
+
+Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from block_sparse_attention_28_amd import inputs, pipeline, seer  # noqa: E402
+from block_sparse_attention_28_amd.workloads import DECODE_WORKLOADS, DECODE_L64K_S90  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "sparse-decode effective KV GB/s (% of HBM peak) + us/step at 90% sparsity"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DECODE_L64K_S90.name, choices=sorted(DECODE_WORKLOADS))
+    ap.add_argument("--layers", type=int, default=4, help="distinct KV caches rotated across steps")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0 = skip)")
+    ap.add_argument("--cpu-sequences", type=int, default=2)
+    return ap.parse_args()
+
+
+class Layer:
+    def __init__(self, w, layer, steps_total, device):
+        self.cache = inputs.decode_cache(w, device, layer=layer)
+        cap = self.cache["k"].shape[2]
+        self.nb_max = cap // w.bs
+        self.kpool = torch.zeros((w.B, w.Hkv, self.nb_max, w.d), dtype=torch.float32, device=device)
+
+
+def decode_bytes(w, seqlens_host):
+    """Algorithmic bytes of one sparse decode launch (kept K/V + tail, q, out, block ids)."""
+    kv = 0
+    for L in seqlens_host:
+        nc, tail = L // w.bs, L % w.bs
+        kv += w.Hkv * (min(w.k_max, nc) * w.bs + tail) * w.d * 2 * 2
+    q_out = 2 * w.B * w.Hq * w.d * 2
+    ids = w.B * w.Hkv * (w.k_max * 4 + 4)
+    return kv, kv + q_out + ids
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    seer.load()
+    dev = torch.device("cuda:0")
+    w = DECODE_WORKLOADS[args.workload]
+    W, K, R = args.warmup, args.steps, max(1, args.layers)
+    total = W + K
+
+    # Per-layer caches with room for the context to grow by one token per R steps.
+    from dataclasses import replace
+    w_run = replace(w, steps_capacity=max(w.steps_capacity, total // R + 1))
+    layers = [Layer(w_run, l, total, dev) for l in range(R)]
+    base_L = layers[0].cache["seqlens"].cpu().to(torch.int64)
+    nb_max = layers[0].nb_max
+    shape = pipeline.DecodeShape(w.B, w.Hq, w.Hkv, w.d, w.bs, w.budget, nb_max, w.gate_dim)
+    plan = pipeline.DecodePlan(shape, dev, num_splits=args.num_splits)
+    for lay in layers:
+        ub, uj = pipeline.full_pool_lists(base_L, w.bs, dev)
+        plan.pool(lay.cache["k"], lay.kpool, ub, uj)
+
+    # Everything a step needs is staged on the device before timing.
+    steps = []
+    for s in range(total):
+        t, l = s // R, s % R
+        L = base_L + t
+        done = [(b, int(L[b]) // w.bs - 1) for b in range(w.B) if int(L[b]) % w.bs == 0 and t > 0]
+        upd = None
+        if done:
+            upd = (torch.tensor([d[0] for d in done], dtype=torch.int32, device=dev),
+                   torch.tensor([d[1] for d in done], dtype=torch.int32, device=dev))
+        steps.append({"layer": l, "seqlens": L.to(torch.int32).to(dev), "L": L.tolist(), "upd": upd,
+                      "q": inputs.decode_query(w, s, dev)})
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+
+    def run_step(s):
+        st = steps[s]
+        lay = layers[st["layer"]]
+        c = lay.cache
+        if st["upd"] is not None:
+            plan.pool(c["k"], lay.kpool, *st["upd"])
+        plan.gate(st["q"], c["wq"], c["wk"], lay.kpool, st["seqlens"])
+        plan.select(st["seqlens"])
+        ev[s][0].record(stream)
+        plan.decode(st["q"], c["k"], c["v"], st["seqlens"])
+        ev[s][1].record(stream)
+
+    for s in range(W):
+        run_step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(W, total):
+        run_step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / K
+    kv_bytes = [decode_bytes(w, steps[s]["L"]) for s in range(W, total)]
+    dec_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(W, total)]
+    mean_kv = sum(b[0] for b in kv_bytes) / K
+    mean_alg = sum(b[1] for b in kv_bytes) / K
+    dec_avg_ms = sum(dec_ms) / K
+    value = mean_kv / (ms_per_step * 1e-3) / 1e9
+    achieved = mean_alg / (dec_avg_ms * 1e-3) / 1e9
+    kept = min(w.k_max, int(base_L.min()) // w.bs)
+    ncb = int(base_L.min()) // w.bs
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "context": int(base_L[0]) if w.L else [int(base_L.min()), int(base_L.max())],
+                   "block_size": w.bs, "budget_tokens": w.budget, "kept_blocks": kept,
+                   "sparsity": round(1.0 - kept / max(ncb, 1), 4), "layers_rotated": R,
+                   "num_splits": plan.num_splits},
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "roofline": {"kernel": "seer_sparse_decode (split + merge)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(mean_alg)},
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, lay, base_L, plan, args):
+    """The fp64 oracle's decode step (gate, select, attention) on a sample of sequences, host cores."""
+    import numpy as np
+
+    import oracle
+    nseq = max(1, min(args.cpu_sequences, w.B))
+    bits = inputs.bf16_bits
+    L = [int(x) for x in base_L[:nseq]]
+    rows = max(L)
+    k = bits(lay.cache["k"][:nseq, :, :rows])
+    v = bits(lay.cache["v"][:nseq, :, :rows])
+    seq = np.array(L, dtype=np.int32)
+    nb = rows // w.bs + 1
+    kp = oracle.pool_cache(k, seq, w.bs, nb)   # built once, outside the timing
+    wq, wk = bits(lay.cache["wq"]), bits(lay.cache["wk"])
+    done, kv, t0 = 0, 0.0, time.perf_counter()
+    while True:
+        q = bits(inputs.decode_query(w, 10_000 + done, "cuda:0")[:nseq])
+        oracle.decode_step(q, k, v, seq, w.bs, w.budget, wq, wk, plan.gate_scale, kp, plan.softmax_scale)
+        kv += sum(w.Hkv * (min(w.k_max, x // w.bs) * w.bs + x % w.bs) * w.d * 4 for x in L)
+        done += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    el = time.perf_counter() - t0
+    cpu_name = platform.processor() or platform.machine()
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_name = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(kv / el / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{nseq} of {w.B} sequences (all {w.Hkv} KV heads), {done} decode steps in {el:.1f} s; "
+                      f"pooled cache built once outside the timing",
+            "us_per_step_equiv": round(el / done * 1e6 * w.B / nseq, 1), "cpu": cpu_name}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,372 @@
+// decode.hip -- split-KV sparse flash-decode over gate-selected KV blocks, and
+// the log-sum-exp merge of the splits.
+//
+// Operation ("SeerAttention-R: Sparse Attention Adaptation for Long
+// Reasoning", abstract): a decoding kernel that reads only the KV blocks the
+// gate kept.  For sequence b, KV head g and each query head h of g's group,
+// softmax attention over T = (kept blocks) + (incomplete tail block).  The
+// tail is always attended: it holds the current token and has no pooled key
+// to be scored with.
+//
+// gfx950 design.  One workgroup (4 waves) per (split, KV head, sequence).  A
+// split owns a contiguous range of "units" (a kept block, or the tail).  For
+// every unit each wave takes a quarter of the block's tokens:
+//   QK : 8 lanes per key row, each lane a 16-byte chunk per 64 head dims;
+//        v_dot2_f32_bf16 with the bf16 query held in registers, then an
+//        8-lane DPP all-reduce.  The key bytes feed all G query heads.
+//   softmax : scores in the log2 domain; one running max per head that is
+//        uniform across the wave, so partial sums need no rescaling when the
+//        wave's lane groups are combined.
+//   PV : probabilities go through LDS to a second layout, one 16-byte value
+//        chunk per lane (a whole 256-byte row per 16 lanes, fully coalesced),
+//        fp32 FMA into G x 8 accumulators per lane.
+// At the end the wave's lane groups and then the 4 waves are combined, and
+// the split writes (unnormalised o, running max, running sum) per head -- or,
+// with a single split, the final normalised output directly.
+#include "seer_device.hpp"
+#include "seer_host.hpp"
+
+#include <math.h>
+
+namespace seer {
+
+struct DecodeArgs {
+    const uint16_t *q;
+    int64_t sq_b, sq_h;
+    const uint16_t *k, *v;
+    int64_t skv_b, skv_h, skv_t;
+    int kv_capacity;
+    const int32_t *seqlens, *block_idx, *n_sel;
+    int k_max, Hq, Hkv, num_splits;
+    float scale_log2;          // softmax_scale * log2(e)
+    float *part_o;             // [B][Hq][S][D]
+    float2 *part_ml;           // [B][Hq][S] (running max in log2 units, running sum)
+    void *out;
+    int out_dtype;
+    float *lse;
+};
+
+template <int D, int BS, int G>
+struct DecodeCfg {
+    static constexpr int NT = 256, NW = 4;
+    static constexpr int CH = D / 8;          // 16-byte chunks per row
+    static constexpr int LPR = 8;             // QK: lanes per key row
+    static constexpr int ROWS = 64 / LPR;     // key rows per wave-wide load
+    static constexpr int CPL = CH / LPR;      // key chunks per lane
+    static constexpr int TPW = BS / NW;       // tokens per wave per unit
+    static constexpr int TPL = TPW / ROWS;    // key rows per lane per unit
+    static constexpr int LPV = CH;            // PV: lanes per value row (one chunk each)
+    static constexpr int ROWSV = 64 / LPV;    // value rows per wave-wide load
+    static constexpr int TPLV = TPW / ROWSV;  // value rows per lane per unit
+    static_assert(CPL >= 1 && TPL >= 1 && TPLV >= 1, "tile shape");
+};
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ void store_out(void *out, int dtype, int64_t i, float x) {
+    if (dtype == SEER_OUT_F32)
+        static_cast<float *>(out)[i] = x;
+    else
+        static_cast<uint16_t *>(out)[i] = f32_to_bf16(x);
+}
+
+template <int D, int BS, int G>
+__global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const DecodeArgs a) {
+    using C = DecodeCfg<D, BS, G>;
+    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane / C::LPR, c = lane % C::LPR;      // QK layout
+    const int rv = lane / C::LPV, cv = lane % C::LPV;    // PV layout
+
+    __shared__ float p_lds[C::NW][C::TPW][G];
+    __shared__ float sm_o[C::NW][G][D];
+    __shared__ float sm_m[C::NW][G], sm_l[C::NW][G];
+
+    int L = a.seqlens[b];
+    L = L < 0 ? 0 : (L > a.kv_capacity ? a.kv_capacity : L);
+    const int nc = L / BS, tail = L - nc * BS;
+    int nsel = a.n_sel[b * a.Hkv + g];
+    const int kcap = a.k_max < nc ? a.k_max : nc;
+    nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
+    const int units = nsel + (tail > 0 ? 1 : 0);
+    const int u0 = (int)(((int64_t)split * units) / a.num_splits);
+    const int u1 = (int)(((int64_t)(split + 1) * units) / a.num_splits);
+
+    // Query rows of the group, bf16 pairs, the chunks this lane multiplies.
+    uint4 qv[G][C::CPL];
+    const uint16_t *qb = a.q + b * a.sq_b + (int64_t)(g * G) * a.sq_h;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < C::CPL; ++i) qv[h][i] = ldg16(qb + h * a.sq_h + (c + i * C::LPR) * 8);
+
+    float m_run[G], l_part[G], o[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_run[h] = -INFINITY;
+        l_part[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    }
+
+    const uint16_t *kb = a.k + b * a.skv_b + g * a.skv_h;
+    const uint16_t *vb = a.v + b * a.skv_b + g * a.skv_h;
+    const int32_t *sel = a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
+    const int wt0 = wave * C::TPW;  // first token of this wave inside a unit
+
+    for (int u = u0; u < u1; ++u) {
+        int tok0, cnt;
+        if (u < nsel) {
+            int blk = sel[u];
+            blk = blk < 0 ? 0 : (blk >= nc ? nc - 1 : blk);
+            tok0 = blk * BS;
+            cnt = BS;
+        } else {
+            tok0 = nc * BS;
+            cnt = tail;
+        }
+        uint4 kr[C::TPL][C::CPL], vr[C::TPLV];
+#pragma unroll
+        for (int t = 0; t < C::TPL; ++t) {
+            int tt = wt0 + r + t * C::ROWS;
+            tt = tt < cnt ? tt : cnt - 1;
+            const uint16_t *row = kb + (int64_t)(tok0 + tt) * a.skv_t;
+#pragma unroll
+            for (int i = 0; i < C::CPL; ++i) kr[t][i] = ldg16(row + (c + i * C::LPR) * 8);
+        }
+#pragma unroll
+        for (int t = 0; t < C::TPLV; ++t) {
+            int tt = wt0 + rv + t * C::ROWSV;
+            tt = tt < cnt ? tt : cnt - 1;
+            vr[t] = ldg16(vb + (int64_t)(tok0 + tt) * a.skv_t + cv * 8);
+        }
+
+        // Scores of this lane group's key rows for every head (log2 domain).
+        float s[C::TPL][G];
+#pragma unroll
+        for (int t = 0; t < C::TPL; ++t) {
+            const bool valid = wt0 + r + t * C::ROWS < cnt;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < C::CPL; ++i) {
+                    acc = dot2_bf16(qv[h][i].x, kr[t][i].x, acc);
+                    acc = dot2_bf16(qv[h][i].y, kr[t][i].y, acc);
+                    acc = dot2_bf16(qv[h][i].z, kr[t][i].z, acc);
+                    acc = dot2_bf16(qv[h][i].w, kr[t][i].w, acc);
+                }
+                acc = group_sum<C::LPR>(acc) * a.scale_log2;
+                s[t][h] = valid ? acc : -INFINITY;
+            }
+        }
+
+        // Wave-uniform running max per head, rescale factors, probabilities.
+        float alpha[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = s[0][h];
+#pragma unroll
+            for (int t = 1; t < C::TPL; ++t) mx = fmax_fast(mx, s[t][h]);
+            mx = cross_group_max<C::LPR>(mx);
+            const float m_new = fmax_fast(m_run[h], mx);
+            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+            alpha[h] = fast_exp2(m_run[h] - m_ref);
+            m_run[h] = m_new;
+            float lsum = 0.f;
+#pragma unroll
+            for (int t = 0; t < C::TPL; ++t) {
+                s[t][h] = fast_exp2(s[t][h] - m_ref);
+                lsum += s[t][h];
+            }
+            l_part[h] = l_part[h] * alpha[h] + lsum;
+        }
+
+        // Probabilities to LDS (one writer per key row), then back in the PV layout.
+        if (c == 0) {
+#pragma unroll
+            for (int t = 0; t < C::TPL; ++t)
+#pragma unroll
+                for (int h = 0; h < G; ++h) p_lds[wave][r + t * C::ROWS][h] = s[t][h];
+        }
+        // LDS accesses of one wave complete in issue order; only this wave reads its slice.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+#pragma unroll
+        for (int t = 0; t < C::TPLV; ++t) {
+            float p[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) p[h] = p_lds[wave][rv + t * C::ROWSV][h];
+            const uint32_t w4[4] = {vr[t].x, vr[t].y, vr[t].z, vr[t].w};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float v0 = bf16lo(w4[e2]), v1 = bf16hi(w4[e2]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    o[h][2 * e2] = fmaf(p[h], v0, o[h][2 * e2]);
+                    o[h][2 * e2 + 1] = fmaf(p[h], v1, o[h][2 * e2 + 1]);
+                }
+            }
+        }
+        // The next unit overwrites p_lds; keep this unit's reads ahead of it.
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // Combine the wave's lane groups: sums only, the max is already wave-uniform.
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l_part[h] = cross_group_sum<C::LPR>(l_part[h]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = cross_group_sum<C::LPV>(o[h][e]);
+    }
+    if (rv == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_o[wave][h][cv * 8 + e] = o[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            sm_m[wave][h] = m_run[h];
+            sm_l[wave][h] = l_part[h];
+        }
+    }
+    __syncthreads();
+
+    // Combine the 4 waves and emit this split's result.
+    for (int i = tid; i < G * D; i += C::NT) {
+        const int h = i / D, e = i % D;
+        float M = sm_m[0][h];
+#pragma unroll
+        for (int w = 1; w < C::NW; ++w) M = fmax_fast(M, sm_m[w][h]);
+        const float Mref = M == -INFINITY ? 0.f : M;
+        float O = 0.f, Ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) {
+            const float f = fast_exp2(sm_m[w][h] - Mref);
+            O = fmaf(sm_o[w][h][e], f, O);
+            Ls = fmaf(sm_l[w][h], f, Ls);
+        }
+        const int hq = g * G + h;
+        const int64_t bh = (int64_t)b * a.Hq + hq;
+        if (a.num_splits == 1) {
+            store_out(a.out, a.out_dtype, bh * D + e, Ls > 0.f ? O / Ls : 0.f);
+            if (e == 0 && a.lse) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+        } else {
+            a.part_o[(bh * a.num_splits + split) * D + e] = O;
+            if (e == 0) a.part_ml[bh * a.num_splits + split] = make_float2(M, Ls);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void sparse_decode_merge_kernel(const float *part_o, const float2 *part_ml,
+                                                                int S, void *out, int out_dtype, float *lse) {
+    const int64_t bh = blockIdx.x;
+    const int e = threadIdx.x;
+    const float2 *ml = part_ml + bh * S;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmax_fast(M, ml[s].x);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float O = 0.f, Ls = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float2 v = ml[s];
+        const float f = fast_exp2(v.x - Mref);
+        Ls = fmaf(v.y, f, Ls);
+        O = fmaf(part_o[(bh * S + s) * D + e], f, O);
+    }
+    store_out(out, out_dtype, bh * D + e, Ls > 0.f ? O / Ls : 0.f);
+    if (e == 0 && lse) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+template <int D, int BS, int G>
+static int launch_decode(const DecodeArgs &a, int B, hipStream_t stream) {
+    dim3 grid(a.num_splits, a.Hkv, B);
+    sparse_decode_split_kernel<D, BS, G><<<grid, 256, 0, stream>>>(a);
+    int st = launch_status();
+    if (st != SEER_OK || a.num_splits == 1) return st;
+    sparse_decode_merge_kernel<D><<<dim3(B * a.Hq), D, 0, stream>>>(a.part_o, a.part_ml, a.num_splits, a.out,
+                                                                     a.out_dtype, a.lse);
+    return launch_status();
+}
+
+template <int D, int BS>
+static int dispatch_group(const DecodeArgs &a, int B, int G, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_decode<D, BS, 1>(a, B, stream);
+        case 2: return launch_decode<D, BS, 2>(a, B, stream);
+        case 4: return launch_decode<D, BS, 4>(a, B, stream);
+        case 8: return launch_decode<D, BS, 8>(a, B, stream);
+    }
+    return SEER_ERR_UNSUPPORTED;
+}
+
+}  // namespace seer
+
+using namespace seer;
+
+extern "C" int seer_sparse_decode_num_splits(int B, int Hkv, int k_max, int block_size, int num_splits) {
+    if (num_splits > 0) return num_splits;
+    if (B <= 0 || Hkv <= 0 || k_max < 0 || block_size <= 0) return 1;
+    // Units per (b, kvh): the kept blocks plus a possible tail.  Aim for about
+    // four units per workgroup, and for at least two workgroups per compute unit.
+    const int units = k_max + 1;
+    int s = (units + 3) / 4;
+    const int cus = device_cu_count();
+    const int64_t pairs = (int64_t)B * Hkv;
+    while (s < units && pairs * s < 2LL * cus) ++s;
+    if (s > units) s = units;
+    if (s > 128) s = 128;
+    return s < 1 ? 1 : s;
+}
+
+extern "C" size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
+                                                    int num_splits) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+    const int s = seer_sparse_decode_num_splits(B, Hkv, k_max, block_size, num_splits);
+    if (s <= 1) return 0;
+    return (size_t)B * Hq * s * ((size_t)d + 2) * sizeof(float);
+}
+
+extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
+                                  const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t, int kv_capacity,
+                                  const int32_t *seqlens, const int32_t *block_idx, const int32_t *n_sel, int k_max,
+                                  int B, int Hq, int Hkv, int d, int block_size, float softmax_scale, int num_splits,
+                                  void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                                  hipStream_t stream) {
+    if (!q || !k || !v || !seqlens || !n_sel || !out) return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || k_max < 0 || kv_capacity < 0 || num_splits < 0)
+        return SEER_ERR_INVALID_ARG;
+    if (k_max > 0 && !block_idx) return SEER_ERR_INVALID_ARG;
+    if (out_dtype != SEER_OUT_BF16 && out_dtype != SEER_OUT_F32) return SEER_ERR_INVALID_ARG;
+    if (skv_t < d || !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !rows_aligned16(k, skv_t) ||
+        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !(softmax_scale == softmax_scale))
+        return SEER_ERR_INVALID_ARG;
+    const int G = Hq / Hkv;
+    if ((d != 64 && d != 128) || (block_size != 64 && block_size != 128) || !pow2_group(G) || G > 8)
+        return SEER_ERR_UNSUPPORTED;
+    const int S = seer_sparse_decode_num_splits(B, Hkv, k_max, block_size, num_splits);
+    const size_t need = seer_sparse_decode_workspace_size(B, Hq, Hkv, d, k_max, block_size, S);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SEER_ERR_WORKSPACE;
+    if (S > 65535) return SEER_ERR_INVALID_ARG;
+
+    DecodeArgs a;
+    a.q = q; a.sq_b = sq_b; a.sq_h = sq_h;
+    a.k = k; a.v = v; a.skv_b = skv_b; a.skv_h = skv_h; a.skv_t = skv_t;
+    a.kv_capacity = kv_capacity;
+    a.seqlens = seqlens; a.block_idx = block_idx; a.n_sel = n_sel;
+    a.k_max = k_max; a.Hq = Hq; a.Hkv = Hkv; a.num_splits = S;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = S > 1 ? reinterpret_cast<float2 *>(static_cast<float *>(workspace) + (size_t)B * Hq * S * d) : nullptr;
+    a.out = out; a.out_dtype = out_dtype; a.lse = lse;
+    if (d == 128) return block_size == 128 ? dispatch_group<128, 128>(a, B, G, stream) : dispatch_group<128, 64>(a, B, G, stream);
+    return block_size == 128 ? dispatch_group<64, 128>(a, B, G, stream) : dispatch_group<64, 64>(a, B, G, stream);
+}

@@ -1,0 +1,113 @@
+// seer_device.hpp -- gfx950 device helpers shared by the library's kernels.
+//
+// Wave64 cross-lane primitives (DPP within 16-lane rows, permlane swaps across
+// rows), bf16 unpacking and the bf16 dot2 builtin.  Nothing here is specific
+// to one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace seer {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc + a.lo * b.lo + a.hi * b.hi with bf16 pairs (v_dot2_f32_bf16, fp32 accumulate).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP controls (GFX9 encoding).
+enum : int {
+    kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141, // lane i <- 7 - i within each 8-lane half row
+    kDppMirror = 0x140,     // lane i <- 15 - i within each 16-lane row
+    kDppRor8 = 0x128,       // lane i <- (i + 8) mod 16 within each row (= xor 8)
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    // bound_ctrl set: every control used here reads a valid lane, and it lets the
+    // compiler fold the move into the consuming VALU op (v_add_f32_dpp).
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float fmax_fast(float a, float b) { return a > b ? a : b; }
+
+// gfx950 permlane swaps exchange 16-lane rows (odd rows of the first operand with
+// even rows of the second) or 32-lane halves.  Fed the same value twice, the two
+// results of every lane are {x, x of the partner row/half} in some order, so a
+// commutative op over them is the pairwise reduction, bitwise identical in both partners.
+__device__ __forceinline__ float sum_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmax_fast(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmax_fast(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over aligned groups of N consecutive lanes (N in 8, 16), result in every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp<kDppMirror>(x);
+    return x;
+}
+
+// Reduce across the 64/STRIDE groups of lanes that share (lane mod STRIDE), STRIDE in {8, 16, 32}.
+template <int STRIDE>
+__device__ __forceinline__ float cross_group_max(float x) {
+    static_assert(STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
+    if constexpr (STRIDE == 8) x = fmax_fast(x, dpp<kDppRor8>(x));
+    if constexpr (STRIDE <= 16) x = max_xor16(x);
+    return max_xor32(x);
+}
+template <int STRIDE>
+__device__ __forceinline__ float cross_group_sum(float x) {
+    static_assert(STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
+    if constexpr (STRIDE == 8) x += dpp<kDppRor8>(x);
+    if constexpr (STRIDE <= 16) x = sum_xor16(x);
+    return sum_xor32(x);
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return cross_group_sum<16>(group_sum<16>(x)); }
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmax_fast(x, dpp<kDppXor1>(x));
+    x = fmax_fast(x, dpp<kDppXor2>(x));
+    x = fmax_fast(x, dpp<kDppHalfMirror>(x));
+    x = fmax_fast(x, dpp<kDppMirror>(x));
+    return cross_group_max<16>(x);
+}
+
+}  // namespace seer

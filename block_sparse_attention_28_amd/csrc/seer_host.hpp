@@ -1,0 +1,28 @@
+// seer_host.hpp -- host-side helpers shared by the C-ABI entry points (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/seer.h"
+
+namespace seer {
+
+// Compute units of the current device, cached once per device id.
+int device_cu_count();
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// bf16 rows of `d` elements with row stride `stride` keep 16-byte alignment.
+inline bool rows_aligned16(const void *base, int64_t stride) {
+    return aligned16(base) && stride >= 0 && (stride * 2) % 16 == 0;
+}
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SEER_OK : SEER_ERR_LAUNCH;
+}
+
+inline bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+}  // namespace seer

@@ -1,0 +1,151 @@
+"""Thin Python binding of the C ABI in include/seer.h (argument marshalling only).
+
+Each function carries the C name, takes torch tensors that already live on
+the GPU, passes their data pointers, strides and the current HIP stream to
+libseer.so, and raises ``SeerError`` on a non-zero status.  Every step of the
+computation runs in the library's gfx950 kernels; there is no fallback: if
+libseer.so is missing or fails to load, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseer.so")
+_lib = None
+
+SEER_OK = 0
+SEER_OUT_BF16 = 0
+SEER_OUT_F32 = 1
+
+# name -> (restype, argtypes); mirrors include/seer.h
+_P, _I, _I64, _F, _SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+SIGNATURES = {
+    "seer_status_string": (C.c_char_p, [_I]),
+    "seer_version": (_I, []),
+    "seer_pool_k_blocks": (_I, [_P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _P]),
+    "seer_gate_workspace_size": (_SZ, [_I, _I, _I]),
+    "seer_gate_scores": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+    "seer_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "seer_sparse_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
+                                _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
+}
+
+
+class SeerError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libseer.so (built in-tree by block_sparse_attention_28_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python -m block_sparse_attention_28_amd.build) first")
+        lib = C.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().seer_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("seer kernels take device tensors")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _call(name: str, *args):
+    st = getattr(load(), name)(*args)
+    if st != SEER_OK:
+        raise SeerError(name, st)
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"expected bfloat16, got {t.dtype}")
+    return t
+
+
+def seer_pool_k_blocks(k, upd_b, upd_blk, kpool, block_size: int, stream=None):
+    """kpool[b, :, j] = mean of block j of k[b] for each listed (b, j).  k [B, Hkv, cap, d] bf16."""
+    _bits(k)
+    B, Hkv, cap, d = k.shape
+    assert kpool.dtype == torch.float32 and kpool.is_contiguous() and kpool.shape[:2] == (B, Hkv)
+    assert upd_b.dtype == torch.int32 and upd_blk.dtype == torch.int32 and upd_b.numel() == upd_blk.numel()
+    _call("seer_pool_k_blocks", _ptr(k), k.stride(0), k.stride(1), k.stride(2), B, Hkv, d, block_size, cap,
+          _ptr(upd_b), _ptr(upd_blk), upd_b.numel(), _ptr(kpool), kpool.shape[2], _stream(stream))
+
+
+def seer_gate_workspace_size(B: int, Hkv: int, d: int) -> int:
+    return load().seer_gate_workspace_size(B, Hkv, d)
+
+
+def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, scores, workspace,
+                     stream=None):
+    """scores [B, Hkv, nb_max] fp32 from q [B, Hq, d], wq/wk [Hkv, dg, d], kpool [B, Hkv, nb_max, d]."""
+    _bits(q), _bits(wq), _bits(wk)
+    B, Hq, d = q.shape
+    Hkv, dg, _ = wq.shape
+    assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
+    _call("seer_gate_scores", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
+          kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), _ptr(scores),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def seer_select_blocks(scores, seqlens, block_size: int, budget_tokens: int, block_idx, n_sel, stream=None):
+    """block_idx [B, H, budget // bs] int32 (ascending, -1 padded), n_sel [B, H] int32."""
+    B, H, nb_max = scores.shape
+    assert scores.is_contiguous() and n_sel.is_contiguous()
+    _call("seer_select_blocks", _ptr(scores), _ptr(seqlens), B, H, nb_max, block_size, budget_tokens,
+          _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel),
+          _stream(stream))
+
+
+def seer_sparse_decode_num_splits(B: int, Hkv: int, k_max: int, block_size: int, num_splits: int = 0) -> int:
+    return load().seer_sparse_decode_num_splits(B, Hkv, k_max, block_size, num_splits)
+
+
+def seer_sparse_decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: int, block_size: int,
+                                      num_splits: int = 0) -> int:
+    return load().seer_sparse_decode_workspace_size(B, Hq, Hkv, d, k_max, block_size, num_splits)
+
+
+def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, softmax_scale: float, out,
+                       lse=None, workspace=None, num_splits: int = 0, stream=None):
+    """out [B, Hq, d] (bf16 or fp32) = attention of q over the kept blocks + tail of k/v [B, Hkv, cap, d]."""
+    _bits(q), _bits(k), _bits(v)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    assert k.stride() == v.stride() and out.is_contiguous()
+    k_max = block_idx.shape[2] if block_idx is not None else 0
+    out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("seer_sparse_decode", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+          k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
+          block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
+          _ptr(lse), _stream(stream))

@@ -1,0 +1,155 @@
+/*
+ * seer.h -- C ABI of the gfx950 (MI355X) gated block-sparse attention library.
+ *
+ * The method: "SeerAttention-R: Sparse Attention Adaptation for Long
+ * Reasoning" (abstract) decodes with a learned gate that scores every KV block
+ * from the current, un-pooled query and the block's pooled key, keeps the
+ * best blocks up to a token budget (64- or 128-token blocks), and runs a
+ * sparse decoding kernel over the kept blocks only.  Its parent,
+ * "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs"
+ * (abstract v1), pools Q and K along the sequence, projects both through
+ * learnable linear layers and multiplies them into block scores that drive a
+ * block-sparse attention kernel for prefill.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps device memory; scratch space is passed
+ *    in as a caller-owned workspace whose minimum size a *_workspace_size
+ *    call reports.
+ *  - bf16 tensors are raw bit patterns (seer_bf16).  Strides are in elements;
+ *    the innermost (head_dim) dimension is always contiguous.  bf16 base
+ *    pointers and row strides must give 16-byte aligned rows.
+ *  - Every call validates its host-side arguments first and returns a
+ *    negative SEER_ERR_* status without launching anything when they are
+ *    invalid.  Otherwise it enqueues its kernels on `stream` and returns
+ *    SEER_OK without synchronising; a launch failure returns SEER_ERR_LAUNCH.
+ *    Device-resident values (context lengths, block ids, counts) cannot be
+ *    checked on the host: the kernels clamp them into range so that a bad
+ *    value yields wrong numbers, never an out-of-bounds access.
+ *  - Calls are thread-safe and keep no state between calls other than a
+ *    per-device cache of the compute-unit count.
+ *  - Head grouping (GQA): query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef SEER_H
+#define SEER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t seer_bf16; /* raw bfloat16 bits */
+
+enum {
+    SEER_OK = 0,
+    SEER_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, bad stride */
+    SEER_ERR_UNSUPPORTED = -2, /* valid but not compiled for (head_dim, block size, group) */
+    SEER_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
+    SEER_ERR_LAUNCH = -4       /* a kernel launch failed (hipGetLastError) */
+};
+
+enum { SEER_OUT_BF16 = 0, SEER_OUT_F32 = 1 };
+
+/* Human-readable name of a status code (static storage). */
+const char *seer_status_string(int status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int seer_version(void);
+
+/*
+ * Pooled-key cache update (the gate's K pooling: SeerAttention v1 abstract
+ * pools K along the sequence, one vector per block; the pooling is the mean).
+ *
+ *   kpool[b][h][j][:] = (1 / block_size) * sum_{t = j*bs}^{j*bs + bs - 1} K[b][h][t][:]
+ *
+ * for every listed (b = upd_b[i], j = upd_blk[i]) and every KV head h.
+ *   k          bf16 [B][Hkv][kv_capacity][d] with strides sk_b, sk_h, sk_t
+ *   upd_b, upd_blk  int32 [n_upd], device; entries out of range are skipped
+ *   kpool      fp32 [B][Hkv][nb_max][d], dense; only listed rows are written
+ * d in {64, 128}; block_size in {64, 128}.  n_upd == 0 is a no-op.
+ * Results are bitwise deterministic, so updating blocks one at a time equals
+ * pooling them all at once.
+ */
+int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t sk_t,
+                       int B, int Hkv, int d, int block_size, int kv_capacity,
+                       const int32_t *upd_b, const int32_t *upd_blk, int n_upd,
+                       float *kpool, int nb_max, hipStream_t stream);
+
+/*
+ * Gate scores of one decode step (SeerAttention-R abstract: the gate keeps
+ * K pooling but drops query pooling, so it reads the current query as is).
+ * For sequence b and KV head g with query heads h in g's group:
+ *
+ *   scores[b][g][j] = mean_h (Wq[g] q[b][h]) . (Wk[g] kpool[b][g][j]) * gate_scale   for j < nc_b
+ *   scores[b][g][j] = -inf                                                            for nc_b <= j < nb_max
+ *
+ * with nc_b = seqlens[b] / block_size complete blocks.  The kernels evaluate
+ * the algebraically equal form (Wk[g]^T Wq[g] qbar) . kpool_j, qbar the group
+ * mean query, in fp32.
+ *   q        bf16 [B][Hq][d] with strides sq_b, sq_h
+ *   wq, wk   bf16 [Hkv][dg][d], dense (the gate's linear layers)
+ *   kpool    fp32 [B][Hkv][nb_max][d], dense (from seer_pool_k_blocks)
+ *   seqlens  int32 [B], device; context length including the current token
+ *   scores   fp32 [B][Hkv][nb_max], dense
+ *   workspace >= seer_gate_workspace_size(B, Hkv, d) bytes
+ * d in {64, 128}; 1 <= dg <= 256; Hq % Hkv == 0.
+ */
+size_t seer_gate_workspace_size(int B, int Hkv, int d);
+int seer_gate_scores(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                     const seer_bf16 *wq, const seer_bf16 *wk, int dg,
+                     const float *kpool, int nb_max, const int32_t *seqlens,
+                     int B, int Hq, int Hkv, int d, int block_size, float gate_scale,
+                     float *scores, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Token-budget block selection (SeerAttention-R abstract: a fixed token
+ * budget at 64/128-token block granularity).  Per (b, head):
+ *   k = min(budget_tokens / block_size, nc_b); keep the k blocks j < nc_b with
+ *   the largest scores, equal scores ordered by the lower block id; write them
+ *   ascending to block_idx[b][h][0..k) and -1 to the rest of the row.
+ *   scores     fp32 [B][H][nb_max] (finite for j < nc_b)
+ *   block_idx  int32 [B][H][budget_tokens / block_size]  (may be NULL when that is 0)
+ *   n_sel      int32 [B][H]
+ * nb_max <= 16384.
+ */
+int seer_select_blocks(const float *scores, const int32_t *seqlens, int B, int H, int nb_max,
+                       int block_size, int budget_tokens, int32_t *block_idx, int32_t *n_sel,
+                       hipStream_t stream);
+
+/*
+ * Sparse decode over the kept blocks (SeerAttention-R abstract: the sparse
+ * decoding kernel reads only the gate's blocks).  For query head h of
+ * sequence b, with KV head g = h / G, the token set is
+ *   T = union over i < n_sel[b][g] of [block_idx[b][g][i] * bs, + bs)  plus the tail [nc_b * bs, seqlens[b])
+ * and the result is softmax attention over T:
+ *   out[b][h] = sum_{t in T} softmax_t(softmax_scale * q[b][h] . K[b][g][t]) V[b][g][t]
+ *   lse[b][h] = log sum_{t in T} exp(softmax_scale * q[b][h] . K[b][g][t])
+ * An empty T gives out = 0 and lse = -inf.  The kept blocks of each (b, g)
+ * are split over `num_splits` workgroups whose partial results are merged by
+ * log-sum-exp (num_splits = 0 picks a count from the shape and the device).
+ *   q          bf16 [B][Hq][d] with strides sq_b, sq_h
+ *   k, v       bf16 [B][Hkv][kv_capacity][d], both with strides skv_b, skv_h, skv_t
+ *   seqlens    int32 [B]; block_idx int32 [B][Hkv][k_max]; n_sel int32 [B][Hkv]
+ *   out        [B][Hq][d] dense, bf16 (SEER_OUT_BF16) or fp32 (SEER_OUT_F32)
+ *   lse        fp32 [B][Hq] or NULL
+ *   workspace  >= seer_sparse_decode_workspace_size(...) bytes (fp32 partials)
+ * d in {64, 128}; block_size in {64, 128}; Hq / Hkv in {1, 2, 4, 8}.
+ */
+int seer_sparse_decode_num_splits(int B, int Hkv, int k_max, int block_size, int num_splits);
+size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
+                                         int num_splits);
+int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                       const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                       int kv_capacity, const int32_t *seqlens, const int32_t *block_idx,
+                       const int32_t *n_sel, int k_max, int B, int Hq, int Hkv, int d, int block_size,
+                       float softmax_scale, int num_splits, void *workspace, size_t workspace_bytes,
+                       void *out, int out_dtype, float *lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SEER_H */

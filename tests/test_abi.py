@@ -1,0 +1,94 @@
+"""The C ABI library: it loads, exports every function include/seer.h declares,
+and rejects invalid host-side arguments with the documented status codes
+before launching anything (no GPU needed: only validation paths run here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seer.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_attention_28_amd import build, seer
+    if not os.path.exists(seer.lib_path()):
+        build.build()
+    return seer.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(seer_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("seer_pool_k_blocks", "seer_gate_scores", "seer_select_blocks", "seer_sparse_decode"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_signatures_cover_the_header(lib):
+    from block_sparse_attention_28_amd import seer
+    assert set(declared_functions()) <= set(seer.SIGNATURES)
+
+
+def test_status_strings(lib):
+    from block_sparse_attention_28_amd import seer
+    assert seer.status_string(0) == "SEER_OK"
+    assert seer.status_string(-3) == "SEER_ERR_WORKSPACE"
+    assert lib.seer_version() >= 100
+
+
+FAKE = C.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+FAKE_ODD = C.c_void_p(0x10002)  # not 16-byte aligned
+NULL = None
+
+
+def decode_args(**over):
+    a = dict(q=FAKE, sq_b=32 * 128, sq_h=128, k=FAKE, v=FAKE, skv_b=8 * 1024 * 128, skv_h=1024 * 128, skv_t=128,
+             cap=1024, seqlens=FAKE, idx=FAKE, n_sel=FAKE, k_max=4, B=2, Hq=32, Hkv=8, d=128, bs=64, scale=0.088,
+             splits=1, ws=NULL, ws_bytes=0, out=FAKE, out_dtype=0, lse=NULL, stream=NULL)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=NULL), -1), (dict(out=NULL), -1), (dict(Hq=30), -1), (dict(B=0), -1),
+    (dict(out_dtype=7), -1), (dict(k=FAKE_ODD), -1), (dict(skv_t=100), -1), (dict(d=96, skv_t=96), -2),
+    (dict(bs=32), -2), (dict(Hq=8 * 16), -2), (dict(splits=4), -3), (dict(splits=4, ws=FAKE, ws_bytes=16), -3),
+    (dict(k_max=4, idx=NULL), -1), (dict(splits=-1), -1),
+])
+def test_sparse_decode_rejects_bad_arguments(lib, over, status):
+    assert lib.seer_sparse_decode(*decode_args(**over)) == status
+
+
+def test_workspace_size_matches_partials(lib):
+    s = lib.seer_sparse_decode_num_splits(16, 8, 51, 128, 13)
+    assert s == 13
+    assert lib.seer_sparse_decode_workspace_size(16, 32, 8, 128, 51, 128, 13) == 16 * 32 * 13 * 130 * 4
+    assert lib.seer_sparse_decode_workspace_size(16, 32, 8, 128, 51, 128, 1) == 0
+
+
+def test_other_calls_reject_bad_arguments(lib):
+    # pool: unsupported block size, then a null cache
+    assert lib.seer_pool_k_blocks(FAKE, 1 << 20, 1 << 16, 128, 2, 8, 128, 32, 1024, FAKE, FAKE, 3, FAKE, 16, NULL) == -2
+    assert lib.seer_pool_k_blocks(FAKE, 1 << 20, 1 << 16, 128, 2, 8, 128, 64, 1024, FAKE, FAKE, 3, NULL, 16, NULL) == -1
+    assert lib.seer_pool_k_blocks(NULL, 0, 0, 0, 2, 8, 128, 64, 1024, NULL, NULL, 0, NULL, 16, NULL) == 0  # no-op
+    # gate: dg too large, missing workspace
+    g = [FAKE, 4096, 128, FAKE, FAKE, 300, FAKE, 16, FAKE, 2, 32, 8, 128, 64, C.c_float(0.1), FAKE, FAKE, 1 << 20, NULL]
+    assert lib.seer_gate_scores(*g) == -1
+    g[5] = 128
+    g[16], g[17] = NULL, 0
+    assert lib.seer_gate_scores(*g) == -3
+    # select: too many blocks for the LDS key buffer; missing outputs
+    assert lib.seer_select_blocks(FAKE, FAKE, 2, 8, 20000, 64, 4096, FAKE, FAKE, NULL) == -2
+    assert lib.seer_select_blocks(FAKE, FAKE, 2, 8, 512, 64, 4096, NULL, FAKE, NULL) == -1

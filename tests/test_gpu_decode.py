@@ -1,0 +1,143 @@
+"""GPU parity of the gated sparse decode path against the fp64 oracle.
+
+Every call goes through the C ABI of libseer.so.  Full comparison on the tiny
+workload; sampled sequences (first, last, one seeded) on the large ones, at
+their full sizes and with the launch configuration the benchmark uses.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_28_amd import inputs, pipeline, seer
+from block_sparse_attention_28_amd.workloads import (DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE, TINY_DECODE,
+                                                     DecodeWorkload)
+
+from gpu_util import build_and_run, check_sequence, oracle_sequence, sample_sequences, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    seer.load()
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 5])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tiny_workload_full(splits, out_dtype):
+    run = build_and_run(TINY_DECODE, num_splits=splits, out_dtype=out_dtype)
+    ref = oracle_sequence(run, 0)
+    st = check_sequence(run, 0, ref)
+    if out_dtype == torch.float32:
+        assert st["max_err"] < 1e-4, st
+    say(f"  tiny splits={splits} max_err={st['max_err']:.3e}")
+
+
+@pytest.mark.parametrize("w", [DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE], ids=lambda w: w.name)
+def test_full_size_pipeline_sampled(w):
+    run = build_and_run(w)
+    worst = 0.0
+    for b in sample_sequences(w.B, seed=w.seed):
+        say(f"  oracle b={b} L={int(run.cache['seqlens'][b])}")
+        st = check_sequence(run, b, oracle_sequence(run, b))
+        worst = max(worst, st["max_err"])
+    say(f"  {w.name}: worst max_err={worst:.3e}")
+
+
+def test_headline_decode_with_oracle_indices():
+    """Decode alone, fed the oracle's own block choice (no gate ties can interfere)."""
+    w = DECODE_L64K_S90
+    run = build_and_run(w)
+    bs_ = sample_sequences(w.B, seed=7)
+    idx = run.plan.block_idx.clone()
+    refs = {}
+    for b in bs_:
+        refs[b] = oracle_sequence(run, b)
+        idx[b] = torch.from_numpy(refs[b]["idx"][0]).to(idx.device)
+    run.plan.decode(run.q, run.cache["k"], run.cache["v"], run.cache["seqlens"], block_idx=idx)
+    torch.cuda.synchronize()
+    out = run.plan.out.float().cpu().double().numpy()
+    for b in bs_:
+        err = np.abs(out[b] - refs[b]["out"][0]).max()
+        assert err <= 1e-2, err
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0, 64])
+def test_split_count_invariance(splits):
+    w = DecodeWorkload(name="splits", B=3, Hq=16, Hkv=4, d=128, bs=64, budget=1024, seed=21, L_range=(900, 5000))
+    run = build_and_run(w, num_splits=splits, out_dtype=torch.float32)
+    for b in range(w.B):
+        st = check_sequence(run, b, oracle_sequence(run, b))
+        assert st["max_err"] < 1e-4, st
+
+
+EDGE = [
+    # (name, B, Hq, Hkv, d, bs, budget, L or range)
+    ("context_below_one_block", 2, 8, 2, 128, 64, 256, 37),
+    ("tail_only_budget_below_block", 2, 8, 2, 128, 64, 32, 300),
+    ("empty_token_set", 1, 4, 1, 64, 64, 0, 256),
+    ("budget_covers_context_dense", 2, 8, 1, 64, 128, 100000, 1000),
+    ("exact_blocks_no_tail", 2, 16, 2, 128, 128, 512, 2048),
+    ("mha_group1", 2, 4, 4, 128, 64, 512, (700, 3000)),
+    ("group2_d64", 3, 8, 4, 64, 64, 384, (100, 2000)),
+    ("group8_bs128", 2, 16, 2, 128, 128, 1024, (3000, 9000)),
+    ("single_token_context", 1, 4, 1, 128, 64, 4096, 1),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(case):
+    name, B, Hq, Hkv, d, bs, budget, L = case
+    w = DecodeWorkload(name=name, B=B, Hq=Hq, Hkv=Hkv, d=d, bs=bs, budget=budget, seed=zlib.crc32(name.encode()) % 1000,
+                       L=L if isinstance(L, int) else None, L_range=L if isinstance(L, tuple) else None)
+    run = build_and_run(w, out_dtype=torch.float32)
+    for b in range(B):
+        check_sequence(run, b, oracle_sequence(run, b))
+    if name == "empty_token_set":
+        assert torch.all(run.plan.out == 0) and torch.all(torch.isneginf(run.plan.lse))
+
+
+def test_pool_incremental_equals_full_rebuild():
+    w = DecodeWorkload(name="pool", B=2, Hq=8, Hkv=2, d=128, bs=64, budget=256, seed=5, L_range=(500, 1500))
+    run = build_and_run(w)
+    inc = torch.zeros_like(run.kpool)
+    ub, uj = pipeline.full_pool_lists(run.cache["seqlens"].cpu(), w.bs)
+    for i in range(ub.numel()):
+        seer.seer_pool_k_blocks(run.cache["k"], ub[i:i + 1], uj[i:i + 1], inc, w.bs)
+    torch.cuda.synchronize()
+    assert torch.equal(inc, run.kpool)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = DECODE_L32K
+    a = build_and_run(w)
+    o1, l1 = a.plan.out.clone(), a.plan.lse.clone()
+    a.plan.step(a.q, a.cache["k"], a.cache["v"], a.cache["seqlens"], a.kpool, a.cache["wq"], a.cache["wk"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, a.plan.out) and torch.equal(l1, a.plan.lse)
+
+
+@pytest.mark.parametrize("nc,k", [(16, 4), (512, 51), (2048, 64), (100, 99), (7, 3), (3000, 64)])
+def test_select_exact_with_ties(nc, k):
+    """Selection on given scores, including exact integer ties: identical to the oracle's rule."""
+    rng = np.random.default_rng(nc + k)
+    B, H, bs = 2, 3, 64
+    scores = rng.integers(-4, 5, size=(B, H, nc)).astype(np.float32)
+    scores[1] = rng.standard_normal((H, nc)).astype(np.float32)
+    seqlens = torch.tensor([nc * bs, nc * bs + 5], dtype=torch.int32, device="cuda")
+    s_dev = torch.from_numpy(scores).cuda()
+    idx = torch.empty((B, H, k), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    seer.seer_select_blocks(s_dev, seqlens, bs, k * bs, idx, n_sel)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.select_blocks(scores[b, h].astype(np.float64), k)
+            assert n_sel[b, h].item() == len(ref)
+            np.testing.assert_array_equal(idx[b, h, :len(ref)].cpu().numpy(), ref)
