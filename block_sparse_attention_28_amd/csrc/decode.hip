@@ -61,7 +61,12 @@ struct DecodeCfg {
     static_assert(CPL >= 1 && TPL >= 1 && TPLV >= 1, "tile shape");
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint4 ldg16_stream(const uint16_t *p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 __device__ __forceinline__ void store_out(void *out, int dtype, int64_t i, float x) {
     if (dtype == SEER_OUT_F32)
@@ -132,13 +137,13 @@ __global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const Decod
             tt = tt < cnt ? tt : cnt - 1;
             const uint16_t *row = kb + (int64_t)(tok0 + tt) * a.skv_t;
 #pragma unroll
-            for (int i = 0; i < C::CPL; ++i) kr[t][i] = ldg16(row + (c + i * C::LPR) * 8);
+            for (int i = 0; i < C::CPL; ++i) kr[t][i] = ldg16_stream(row + (c + i * C::LPR) * 8);
         }
 #pragma unroll
         for (int t = 0; t < C::TPLV; ++t) {
             int tt = wt0 + rv + t * C::ROWSV;
             tt = tt < cnt ? tt : cnt - 1;
-            vr[t] = ldg16(vb + (int64_t)(tok0 + tt) * a.skv_t + cv * 8);
+            vr[t] = ldg16_stream(vb + (int64_t)(tok0 + tt) * a.skv_t + cv * 8);
         }
 
         // Scores of this lane group's key rows for every head (log2 domain).
@@ -266,24 +271,44 @@ __global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const Decod
     }
 }
 
+// One workgroup per (b, query head): the split maxima and sums are loaded in
+// parallel, the per-split weights 2^(m_s - M) staged in LDS, then every thread
+// sums its output column over the splits with independent loads.
+constexpr int kMaxSplits = 128;
+
 template <int D>
-__global__ __launch_bounds__(D) void sparse_decode_merge_kernel(const float *part_o, const float2 *part_ml,
-                                                                int S, void *out, int out_dtype, float *lse) {
+__global__ __launch_bounds__(128) void sparse_decode_merge_kernel(const float *part_o, const float2 *part_ml,
+                                                                  int S, void *out, int out_dtype, float *lse) {
+    __shared__ float w_s[kMaxSplits];
+    __shared__ float red[2][2];
     const int64_t bh = blockIdx.x;
-    const int e = threadIdx.x;
-    const float2 *ml = part_ml + bh * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmax_fast(M, ml[s].x);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float2 v = tid < S ? part_ml[bh * S + tid] : make_float2(-INFINITY, 0.f);
+    float M = wave_max(v.x);
+    if (lane == 0) red[0][wave] = M;
+    __syncthreads();
+    M = fmax_fast(red[0][0], red[0][1]);
     const float Mref = M == -INFINITY ? 0.f : M;
-    float O = 0.f, Ls = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float2 v = ml[s];
-        const float f = fast_exp2(v.x - Mref);
-        Ls = fmaf(v.y, f, Ls);
-        O = fmaf(part_o[(bh * S + s) * D + e], f, O);
+    const float f = tid < S ? fast_exp2(v.x - Mref) : 0.f;
+    if (tid < S) w_s[tid] = f;
+    float Ls = wave_sum(v.y * f);
+    if (lane == 0) red[1][wave] = Ls;
+    __syncthreads();
+    Ls = red[1][0] + red[1][1];
+    if (tid >= D) return;
+    const float *po = part_o + bh * S * D + tid;
+    float O = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= S; sp += 8) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = po[(int64_t)(sp + i) * D];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) O = fmaf(x[i], w_s[sp + i], O);
     }
-    store_out(out, out_dtype, bh * D + e, Ls > 0.f ? O / Ls : 0.f);
-    if (e == 0 && lse) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    for (; sp < S; ++sp) O = fmaf(po[(int64_t)sp * D], w_s[sp], O);
+    store_out(out, out_dtype, bh * D + tid, Ls > 0.f ? O / Ls : 0.f);
+    if (tid == 0 && lse) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 template <int D, int BS, int G>
@@ -292,7 +317,7 @@ static int launch_decode(const DecodeArgs &a, int B, hipStream_t stream) {
     sparse_decode_split_kernel<D, BS, G><<<grid, 256, 0, stream>>>(a);
     int st = launch_status();
     if (st != SEER_OK || a.num_splits == 1) return st;
-    sparse_decode_merge_kernel<D><<<dim3(B * a.Hq), D, 0, stream>>>(a.part_o, a.part_ml, a.num_splits, a.out,
+    sparse_decode_merge_kernel<D><<<dim3(B * a.Hq), 128, 0, stream>>>(a.part_o, a.part_ml, a.num_splits, a.out,
                                                                      a.out_dtype, a.lse);
     return launch_status();
 }
@@ -313,18 +338,18 @@ static int dispatch_group(const DecodeArgs &a, int B, int G, hipStream_t stream)
 using namespace seer;
 
 extern "C" int seer_sparse_decode_num_splits(int B, int Hkv, int k_max, int block_size, int num_splits) {
-    if (num_splits > 0) return num_splits;
+    if (num_splits > 0) return num_splits < kMaxSplits ? num_splits : kMaxSplits;
     if (B <= 0 || Hkv <= 0 || k_max < 0 || block_size <= 0) return 1;
-    // Units per (b, kvh): the kept blocks plus a possible tail.  Aim for about
-    // four units per workgroup, and for at least two workgroups per compute unit.
+    // Units per (b, kvh): the kept blocks plus a possible tail.  Long-running
+    // workgroups stream best: aim for about two workgroups per compute unit,
+    // all resident at once, each with as many units as that leaves.
     const int units = k_max + 1;
-    int s = (units + 3) / 4;
     const int cus = device_cu_count();
     const int64_t pairs = (int64_t)B * Hkv;
-    while (s < units && pairs * s < 2LL * cus) ++s;
+    int64_t s = (2LL * cus + pairs - 1) / pairs;
     if (s > units) s = units;
-    if (s > 128) s = 128;
-    return s < 1 ? 1 : s;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : (int)s;
 }
 
 extern "C" size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
@@ -355,7 +380,7 @@ extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h
     const int S = seer_sparse_decode_num_splits(B, Hkv, k_max, block_size, num_splits);
     const size_t need = seer_sparse_decode_workspace_size(B, Hq, Hkv, d, k_max, block_size, S);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SEER_ERR_WORKSPACE;
-    if (S > 65535) return SEER_ERR_INVALID_ARG;
+    if (S > kMaxSplits) return SEER_ERR_INVALID_ARG;
 
     DecodeArgs a;
     a.q = q; a.sq_b = sq_b; a.sq_h = sq_h;

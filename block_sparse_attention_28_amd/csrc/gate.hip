@@ -8,70 +8,54 @@
 // selection per KV head, the block score is the mean of the group's query-head
 // scores; because every step is linear,
 //     mean_h (Wq q_h) . (Wk kp_j) = (Wk^T Wq qbar) . kp_j ,   qbar = mean_h q_h,
-// so a tiny kernel forms u = gate_scale * Wk^T (Wq qbar) once per (b, g) and
-// the bandwidth-bound kernel streams the fp32 pooled keys once:
-//     score_j = u . kp_j.
+// so each workgroup forms u = gate_scale * Wk^T (Wq qbar) for its (b, g) and
+// then streams fp32 pooled keys once: score_j = u . kp_j.
+//
+// One launch.  A workgroup owns RPB consecutive pooled-key rows of one (b, g):
+// it issues all of their loads first (16 bytes per lane, 4 rows in flight per
+// thread and per load instruction), computes u from the L2-resident gate
+// weights while those loads are in flight, then finishes the dot products
+// with 32-lane DPP/permlane reductions.
 #include "seer_device.hpp"
 #include "seer_host.hpp"
 
 namespace seer {
 
-// u[b][g][:] = gate_scale * Wk[g]^T (Wq[g] qbar).  One workgroup per (g, b).
 template <int D>
-__global__ __launch_bounds__(256) void gate_u_kernel(const uint16_t *q, int64_t sq_b, int64_t sq_h,
-                                                     const uint16_t *wq, const uint16_t *wk, int dg, int G, int Hkv,
-                                                     float gate_scale, float *u) {
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    __shared__ float qbar[D];
-    __shared__ float a_s[256];
-    if (tid < D) {
-        const uint16_t *qg = q + b * sq_b + (int64_t)(g * G) * sq_h + tid;
-        float s = 0.f;
-        for (int h = 0; h < G; ++h) s += __uint_as_float((uint32_t)qg[h * sq_h] << 16);
-        qbar[tid] = s / (float)G;
-    }
-    __syncthreads();
-    const uint16_t *wqg = wq + (int64_t)g * dg * D;
-    for (int rr = wave; rr < dg; rr += 4) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = lane; e < D; e += 64) s = fmaf(__uint_as_float((uint32_t)wqg[(int64_t)rr * D + e] << 16), qbar[e], s);
-        s = wave_sum(s);
-        if (lane == 0) a_s[rr] = s;
-    }
-    __syncthreads();
-    if (tid < D) {
-        const uint16_t *wkg = wk + (int64_t)g * dg * D + tid;
-        float s = 0.f;
-        for (int rr = 0; rr < dg; ++rr) s = fmaf(__uint_as_float((uint32_t)wkg[(int64_t)rr * D] << 16), a_s[rr], s);
-        u[((int64_t)b * Hkv + g) * D + tid] = gate_scale * s;
-    }
-}
-
-// scores[b][g][j] = u[b][g] . kpool[b][g][j] for j < nc_b, -inf for nc_b <= j < nb_max.
-// LPR lanes per pooled-key row (16 bytes = 4 floats each); RPB rows per workgroup.
-template <int D>
-struct GateScoreCfg {
-    static constexpr int LPR = D / 4;           // 32 (d=128) or 16 (d=64)
-    static constexpr int ROWS = 256 / LPR;      // rows per workgroup-wide load
-    static constexpr int ITER = 8;              // loads in flight per thread
-    static constexpr int RPB = ROWS * ITER;     // rows per workgroup
+struct GateCfg {
+    static constexpr int LPR = D / 4;        // lanes per pooled-key row (4 floats each)
+    static constexpr int ROWS = 256 / LPR;   // rows per workgroup-wide load: 8 or 16
+    static constexpr int ITER = 16;          // row loads in flight per thread
+    static constexpr int RPB = ROWS * ITER;  // rows per workgroup
+    static constexpr int CH = D / 8;         // 16-byte bf16 chunks per weight row: 16 or 8
+    static constexpr int RG = 256 / CH;      // weight-row groups: 16 or 32
 };
 
+__device__ __forceinline__ void unpack8(const uint4 w, float *f) {
+    f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
+    f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void gate_scores_kernel(const float *kpool, int nb_max, const int32_t *seqlens,
-                                                          int Hkv, int block_size, const float *u, float *scores) {
-    using C = GateScoreCfg<D>;
-    const int pair = blockIdx.y;  // b * Hkv + g
-    const int b = pair / Hkv;
+__global__ __launch_bounds__(256) void gate_scores_kernel(const uint16_t *q, int64_t sq_b, int64_t sq_h,
+                                                          const uint16_t *wq, const uint16_t *wk, int dg, int G,
+                                                          int Hkv, float gate_scale, const float *kpool, int nb_max,
+                                                          const int32_t *seqlens, int block_size, float *scores) {
+    using C = GateCfg<D>;
+    const int pair = blockIdx.y, b = pair / Hkv, g = pair % Hkv;
     const int tid = threadIdx.x, lr = tid / C::LPR, lc = tid % C::LPR;
     int L = seqlens[b];
     L = L < 0 ? 0 : L;
     int nc = L / block_size;
     nc = nc > nb_max ? nb_max : nc;
     const int j0 = blockIdx.x * C::RPB;
-    const float4 uu = reinterpret_cast<const float4 *>(u + (int64_t)pair * D)[lc];
+    float *srow = scores + (int64_t)pair * nb_max;
+    if (j0 >= nc) {  // nothing complete here: only -inf to write
+        for (int j = j0 + tid; j < j0 + C::RPB && j < nb_max; j += 256) srow[j] = -INFINITY;
+        return;
+    }
+
+    // 1. Pooled-key rows of this workgroup, all loads issued up front.
     const float *kp = kpool + (int64_t)pair * nb_max * D;
     float4 x[C::ITER];
 #pragma unroll
@@ -79,6 +63,86 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(const float *kpool, in
         const int j = j0 + lr + it * C::ROWS;
         x[it] = j < nc ? reinterpret_cast<const float4 *>(kp + (int64_t)j * D)[lc] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+
+    // 2. u = gate_scale * Wk^T (Wq qbar) for (b, g).
+    __shared__ float a_s[256];
+    __shared__ float u_part[C::RG][D];
+    __shared__ float u_s[D];
+    const int c = tid % C::CH, rg = tid / C::CH;
+    // Each thread owns the 16-byte column chunk c of weight rows rg, rg + RG, ...,
+    // taken 8 rows at a time with all 8 loads issued before any is used.
+    constexpr int WB = 8;
+    const uint16_t *qg = q + b * sq_b + (int64_t)(g * G) * sq_h + c * 8;
+    float qb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int h0 = 0; h0 < G; h0 += 4) {
+        uint4 qw[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            qw[h] = h0 + h < G ? *reinterpret_cast<const uint4 *>(qg + (h0 + h) * sq_h) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            float f[8];
+            unpack8(qw[h], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qb[e] += f[e];
+        }
+    }
+    const float inv_g = 1.0f / (float)G;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[e] *= inv_g;
+    const uint16_t *wqg = wq + (int64_t)g * dg * D + c * 8;
+    const uint16_t *wkg = wk + (int64_t)g * dg * D + c * 8;
+    for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {  // a[r] = Wq[r] . qbar
+        uint4 w[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+            const int r = r0 + rg + i * C::RG;
+            w[i] = r < dg ? *reinterpret_cast<const uint4 *>(wqg + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+            const int r = r0 + rg + i * C::RG;
+            float f[8];
+            unpack8(w[i], f);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(f[e], qb[e], s);
+            s = group_sum<C::CH>(s);  // all CH lanes of a row group share r
+            if (c == 0 && r < dg) a_s[r] = s;
+        }
+    }
+    __syncthreads();
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {  // u += a[r] * Wk[r]
+        uint4 w[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+            const int r = r0 + rg + i * C::RG;
+            w[i] = r < dg ? *reinterpret_cast<const uint4 *>(wkg + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+            const int r = r0 + rg + i * C::RG;
+            float f[8];
+            unpack8(w[i], f);
+            const float ar = r < dg ? a_s[r] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(ar, f[e], acc[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u_part[rg][c * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < C::RG; ++r) s += u_part[r][tid];
+        u_s[tid] = s * gate_scale;
+    }
+    __syncthreads();
+
+    // 3. score_j = u . kp_j
+    const float4 uu = reinterpret_cast<const float4 *>(u_s)[lc];
 #pragma unroll
     for (int it = 0; it < C::ITER; ++it) {
         const int j = j0 + lr + it * C::ROWS;
@@ -88,7 +152,7 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(const float *kpool, in
         s = fmaf(uu.w, x[it].w, s);
         s = group_sum<16>(s);
         if constexpr (C::LPR == 32) s = sum_xor16(s);
-        if (lc == 0 && j < nb_max) scores[(int64_t)pair * nb_max + j] = j < nc ? s : -INFINITY;
+        if (lc == 0 && j < nb_max) srow[j] = j < nc ? s : -INFINITY;
     }
 }
 
@@ -96,38 +160,28 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(const float *kpool, in
 
 using namespace seer;
 
-extern "C" size_t seer_gate_workspace_size(int B, int Hkv, int d) {
-    if (B <= 0 || Hkv <= 0 || d <= 0) return 0;
-    return (size_t)B * Hkv * d * sizeof(float);
-}
-
 extern "C" int seer_gate_scores(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *wq,
                                 const seer_bf16 *wk, int dg, const float *kpool, int nb_max, const int32_t *seqlens,
                                 int B, int Hq, int Hkv, int d, int block_size, float gate_scale, float *scores,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                hipStream_t stream) {
     if (!q || !wq || !wk || !seqlens || !scores) return SEER_ERR_INVALID_ARG;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || nb_max < 0 || block_size <= 0 || dg < 1 || dg > 256 ||
-        sq_h < 0 || sq_b < 0 || !(gate_scale == gate_scale))
+        !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !aligned16(wq) || !aligned16(wk) ||
+        !(gate_scale == gate_scale))
         return SEER_ERR_INVALID_ARG;
     if (nb_max > 0 && (!kpool || !aligned16(kpool))) return SEER_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return SEER_ERR_UNSUPPORTED;
-    const size_t need = seer_gate_workspace_size(B, Hkv, d);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SEER_ERR_WORKSPACE;
-    if (Hkv > 65535 || B > 65535 || (int64_t)B * Hkv > 65535) return SEER_ERR_INVALID_ARG;
-    float *u = static_cast<float *>(workspace);
+    if ((int64_t)B * Hkv > 65535) return SEER_ERR_INVALID_ARG;
+    if (nb_max == 0) return SEER_OK;
     const int G = Hq / Hkv;
-    if (d == 128)
-        gate_u_kernel<128><<<dim3(Hkv, B), 256, 0, stream>>>(q, sq_b, sq_h, wq, wk, dg, G, Hkv, gate_scale, u);
-    else
-        gate_u_kernel<64><<<dim3(Hkv, B), 256, 0, stream>>>(q, sq_b, sq_h, wq, wk, dg, G, Hkv, gate_scale, u);
-    int st = launch_status();
-    if (st != SEER_OK || nb_max == 0) return st;
     if (d == 128) {
-        dim3 grid((nb_max + GateScoreCfg<128>::RPB - 1) / GateScoreCfg<128>::RPB, B * Hkv);
-        gate_scores_kernel<128><<<grid, 256, 0, stream>>>(kpool, nb_max, seqlens, Hkv, block_size, u, scores);
+        dim3 grid((nb_max + GateCfg<128>::RPB - 1) / GateCfg<128>::RPB, B * Hkv);
+        gate_scores_kernel<128><<<grid, 256, 0, stream>>>(q, sq_b, sq_h, wq, wk, dg, G, Hkv, gate_scale, kpool,
+                                                          nb_max, seqlens, block_size, scores);
     } else {
-        dim3 grid((nb_max + GateScoreCfg<64>::RPB - 1) / GateScoreCfg<64>::RPB, B * Hkv);
-        gate_scores_kernel<64><<<grid, 256, 0, stream>>>(kpool, nb_max, seqlens, Hkv, block_size, u, scores);
+        dim3 grid((nb_max + GateCfg<64>::RPB - 1) / GateCfg<64>::RPB, B * Hkv);
+        gate_scores_kernel<64><<<grid, 256, 0, stream>>>(q, sq_b, sq_h, wq, wk, dg, G, Hkv, gate_scale, kpool,
+                                                         nb_max, seqlens, block_size, scores);
     }
     return launch_status();
 }

@@ -27,9 +27,12 @@ __global__ __launch_bounds__(256) void pool_k_kernel(const uint16_t *k, int64_t 
     const int c = tid % CH, rg = tid / CH;
     const uint16_t *base = k + b * sk_b + h * sk_h + (int64_t)j * BS * sk_t + c * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint4 rows[BS / RG];
 #pragma unroll
-    for (int t = rg; t < BS; t += RG) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(base + (int64_t)t * sk_t);
+    for (int i = 0; i < BS / RG; ++i) rows[i] = *reinterpret_cast<const uint4 *>(base + (int64_t)(rg + i * RG) * sk_t);
+#pragma unroll
+    for (int i = 0; i < BS / RG; ++i) {
+        const uint4 w = rows[i];
         acc[0] += bf16lo(w.x); acc[1] += bf16hi(w.x);
         acc[2] += bf16lo(w.y); acc[3] += bf16hi(w.y);
         acc[4] += bf16lo(w.z); acc[5] += bf16hi(w.z);

@@ -42,8 +42,6 @@ class DecodePlan:
         self.gate_scale = 1.0 / math.sqrt(s.dg) if gate_scale is None else gate_scale
         self.softmax_scale = 1.0 / math.sqrt(s.d) if softmax_scale is None else softmax_scale
         self.scores = torch.empty((s.B, s.Hkv, max(s.nb_max, 1)), dtype=torch.float32, device=dev)
-        gws = seer.seer_gate_workspace_size(s.B, s.Hkv, s.d)
-        self.gate_ws = torch.empty((max(gws, 16) + 3) // 4, dtype=torch.float32, device=dev)
         self.block_idx = torch.empty((s.B, s.Hkv, s.k_max), dtype=torch.int32, device=dev)
         self.n_sel = torch.empty((s.B, s.Hkv), dtype=torch.int32, device=dev)
         self.num_splits = seer.seer_sparse_decode_num_splits(s.B, s.Hkv, s.k_max, s.bs, num_splits)
@@ -57,7 +55,7 @@ class DecodePlan:
 
     def gate(self, q, wq, wk, kpool, seqlens, stream=None):
         seer.seer_gate_scores(q, wq, wk, kpool, seqlens, self.shape.bs, self.gate_scale, self.scores,
-                              self.gate_ws, stream=stream)
+                              stream=stream)
 
     def select(self, seqlens, stream=None):
         seer.seer_select_blocks(self.scores, seqlens, self.shape.bs, self.shape.budget, self.block_idx,

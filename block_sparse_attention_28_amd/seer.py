@@ -27,8 +27,7 @@ SIGNATURES = {
     "seer_status_string": (C.c_char_p, [_I]),
     "seer_version": (_I, []),
     "seer_pool_k_blocks": (_I, [_P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _P]),
-    "seer_gate_workspace_size": (_SZ, [_I, _I, _I]),
-    "seer_gate_scores": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+    "seer_gate_scores": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
     "seer_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "seer_sparse_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -101,12 +100,7 @@ def seer_pool_k_blocks(k, upd_b, upd_blk, kpool, block_size: int, stream=None):
           _ptr(upd_b), _ptr(upd_blk), upd_b.numel(), _ptr(kpool), kpool.shape[2], _stream(stream))
 
 
-def seer_gate_workspace_size(B: int, Hkv: int, d: int) -> int:
-    return load().seer_gate_workspace_size(B, Hkv, d)
-
-
-def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, scores, workspace,
-                     stream=None):
+def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, scores, stream=None):
     """scores [B, Hkv, nb_max] fp32 from q [B, Hq, d], wq/wk [Hkv, dg, d], kpool [B, Hkv, nb_max, d]."""
     _bits(q), _bits(wq), _bits(wk)
     B, Hq, d = q.shape
@@ -114,7 +108,7 @@ def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: flo
     assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
     _call("seer_gate_scores", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
           kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), _ptr(scores),
-          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+          _stream(stream))
 
 
 def seer_select_blocks(scores, seqlens, block_size: int, budget_tokens: int, block_idx, n_sel, stream=None):

@@ -87,23 +87,21 @@ int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t s
  *   scores[b][g][j] = mean_h (Wq[g] q[b][h]) . (Wk[g] kpool[b][g][j]) * gate_scale   for j < nc_b
  *   scores[b][g][j] = -inf                                                            for nc_b <= j < nb_max
  *
- * with nc_b = seqlens[b] / block_size complete blocks.  The kernels evaluate
+ * with nc_b = seqlens[b] / block_size complete blocks.  The kernel evaluates
  * the algebraically equal form (Wk[g]^T Wq[g] qbar) . kpool_j, qbar the group
- * mean query, in fp32.
+ * mean query, in fp32, in a single launch.
  *   q        bf16 [B][Hq][d] with strides sq_b, sq_h
  *   wq, wk   bf16 [Hkv][dg][d], dense (the gate's linear layers)
  *   kpool    fp32 [B][Hkv][nb_max][d], dense (from seer_pool_k_blocks)
  *   seqlens  int32 [B], device; context length including the current token
  *   scores   fp32 [B][Hkv][nb_max], dense
- *   workspace >= seer_gate_workspace_size(B, Hkv, d) bytes
- * d in {64, 128}; 1 <= dg <= 256; Hq % Hkv == 0.
+ * d in {64, 128}; 1 <= dg <= 256; Hq % Hkv == 0; B * Hkv <= 65535.
  */
-size_t seer_gate_workspace_size(int B, int Hkv, int d);
 int seer_gate_scores(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                      const seer_bf16 *wq, const seer_bf16 *wk, int dg,
                      const float *kpool, int nb_max, const int32_t *seqlens,
                      int B, int Hq, int Hkv, int d, int block_size, float gate_scale,
-                     float *scores, void *workspace, size_t workspace_bytes, hipStream_t stream);
+                     float *scores, hipStream_t stream);
 
 /*
  * Token-budget block selection (SeerAttention-R abstract: a fixed token
@@ -114,7 +112,7 @@ int seer_gate_scores(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
  *   scores     fp32 [B][H][nb_max] (finite for j < nc_b)
  *   block_idx  int32 [B][H][budget_tokens / block_size]  (may be NULL when that is 0)
  *   n_sel      int32 [B][H]
- * nb_max <= 16384.
+ * nb_max <= 16128.
  */
 int seer_select_blocks(const float *scores, const int32_t *seqlens, int B, int H, int nb_max,
                        int block_size, int budget_tokens, int32_t *block_idx, int32_t *n_sel,
@@ -129,14 +127,16 @@ int seer_select_blocks(const float *scores, const int32_t *seqlens, int B, int H
  *   out[b][h] = sum_{t in T} softmax_t(softmax_scale * q[b][h] . K[b][g][t]) V[b][g][t]
  *   lse[b][h] = log sum_{t in T} exp(softmax_scale * q[b][h] . K[b][g][t])
  * An empty T gives out = 0 and lse = -inf.  The kept blocks of each (b, g)
- * are split over `num_splits` workgroups whose partial results are merged by
- * log-sum-exp (num_splits = 0 picks a count from the shape and the device).
+ * are split over `num_splits` workgroups (at most 128) whose partial results a
+ * second kernel merges by log-sum-exp (num_splits = 0 picks a count from the
+ * shape and the device).
  *   q          bf16 [B][Hq][d] with strides sq_b, sq_h
  *   k, v       bf16 [B][Hkv][kv_capacity][d], both with strides skv_b, skv_h, skv_t
  *   seqlens    int32 [B]; block_idx int32 [B][Hkv][k_max]; n_sel int32 [B][Hkv]
  *   out        [B][Hq][d] dense, bf16 (SEER_OUT_BF16) or fp32 (SEER_OUT_F32)
  *   lse        fp32 [B][Hq] or NULL
- *   workspace  >= seer_sparse_decode_workspace_size(...) bytes (fp32 partials)
+ *   workspace  >= seer_sparse_decode_workspace_size(...) bytes of fp32 partial
+ *              results (none is needed, size 0, when a single split is used)
  * d in {64, 128}; block_size in {64, 128}; Hq / Hkv in {1, 2, 4, 8}.
  */
 int seer_sparse_decode_num_splits(int B, int Hkv, int k_max, int block_size, int num_splits);

@@ -64,7 +64,7 @@ def decode_args(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(q=NULL), -1), (dict(out=NULL), -1), (dict(Hq=30), -1), (dict(B=0), -1),
     (dict(out_dtype=7), -1), (dict(k=FAKE_ODD), -1), (dict(skv_t=100), -1), (dict(d=96, skv_t=96), -2),
-    (dict(bs=32), -2), (dict(Hq=8 * 16), -2), (dict(splits=4), -3), (dict(splits=4, ws=FAKE, ws_bytes=16), -3),
+    (dict(bs=32), -2), (dict(Hq=8 * 16), -2), (dict(splits=4), -3), (dict(splits=4, ws=FAKE, ws_bytes=16), -3), (dict(splits=4, ws=FAKE_ODD, ws_bytes=1 << 30), -3),
     (dict(k_max=4, idx=NULL), -1), (dict(splits=-1), -1),
 ])
 def test_sparse_decode_rejects_bad_arguments(lib, over, status):
@@ -83,12 +83,14 @@ def test_other_calls_reject_bad_arguments(lib):
     assert lib.seer_pool_k_blocks(FAKE, 1 << 20, 1 << 16, 128, 2, 8, 128, 32, 1024, FAKE, FAKE, 3, FAKE, 16, NULL) == -2
     assert lib.seer_pool_k_blocks(FAKE, 1 << 20, 1 << 16, 128, 2, 8, 128, 64, 1024, FAKE, FAKE, 3, NULL, 16, NULL) == -1
     assert lib.seer_pool_k_blocks(NULL, 0, 0, 0, 2, 8, 128, 64, 1024, NULL, NULL, 0, NULL, 16, NULL) == 0  # no-op
-    # gate: dg too large, missing workspace
-    g = [FAKE, 4096, 128, FAKE, FAKE, 300, FAKE, 16, FAKE, 2, 32, 8, 128, 64, C.c_float(0.1), FAKE, FAKE, 1 << 20, NULL]
+    # gate: dg too large, misaligned query, unsupported head_dim
+    g = [FAKE, 4096, 128, FAKE, FAKE, 300, FAKE, 16, FAKE, 2, 32, 8, 128, 64, C.c_float(0.1), FAKE, NULL]
     assert lib.seer_gate_scores(*g) == -1
     g[5] = 128
-    g[16], g[17] = NULL, 0
-    assert lib.seer_gate_scores(*g) == -3
+    g[0] = FAKE_ODD
+    assert lib.seer_gate_scores(*g) == -1
+    g[0], g[12], g[1], g[2] = FAKE, 96, 32 * 96, 96
+    assert lib.seer_gate_scores(*g) == -2
     # select: too many blocks for the LDS key buffer; missing outputs
     assert lib.seer_select_blocks(FAKE, FAKE, 2, 8, 20000, 64, 4096, FAKE, FAKE, NULL) == -2
     assert lib.seer_select_blocks(FAKE, FAKE, 2, 8, 512, 64, 4096, NULL, FAKE, NULL) == -1
