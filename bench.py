@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0 = skip)")
     ap.add_argument("--cpu-sequences", type=int, default=2)
+    ap.add_argument("--prefill-steps", type=int, default=5, help="block-sparse prefill timing (0 = skip)")
     return ap.parse_args()
 
 
@@ -195,7 +196,64 @@ def main():
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)
+    if args.prefill_steps > 0:
+        del layers
+        torch.cuda.empty_cache()
+        line["secondary_path"] = bench_prefill(args.prefill_steps, dev)
     print(json.dumps(line), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(counts, bs, d):
+    """Algorithmic flops of block-sparse causal attention: 4*bs*bs*d per kept off-diagonal
+    block (QK^T and PV), 4*(bs*(bs+1)/2)*d per diagonal block (its causal half)."""
+    kept = int(counts.sum())
+    diag = counts.numel()
+    return (kept - diag) * 4 * bs * bs * d + diag * 4 * (bs * (bs + 1) // 2) * d
+
+
+def bench_prefill(steps, dev):
+    """Gate + MFMA attention of the 32k-token block-sparse causal prefill (keep 1/10)."""
+    from block_sparse_attention_28_amd.workloads import PREFILL_L32K as pw
+    x = inputs.prefill_inputs(pw, dev)
+    nb = (pw.L + pw.bs - 1) // pw.bs
+    kmax = seer.seer_block_sparse_prefill_kmax_row(pw.L, pw.bs, pw.keep_num, pw.keep_den)
+    blocks = torch.empty((pw.B, pw.H, nb, kmax), dtype=torch.int32, device=dev)
+    counts = torch.empty((pw.B, pw.H, nb), dtype=torch.int32, device=dev)
+    wsb = seer.seer_block_sparse_prefill_workspace_size(pw.B, pw.H, pw.L, pw.d, pw.bs, pw.gate_dim)
+    ws = torch.empty((wsb + 3) // 4, dtype=torch.float32, device=dev)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((pw.B, pw.H, pw.L), dtype=torch.float32, device=dev)
+    gs, ss = 1 / math.sqrt(pw.gate_dim), 1 / math.sqrt(pw.d)
+
+    def call(given):
+        seer.seer_block_sparse_prefill(x["q"], x["k"], x["v"], pw.bs, x["wq"], x["wk"], gs, pw.keep_num,
+                                       pw.keep_den, blocks, counts, ss, out, lse, ws, use_given_blocks=given)
+
+    def timed(given):
+        for _ in range(2):
+            call(given)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call(given)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us_total = timed(False)
+    us_attn = timed(True)
+    flops = prefill_flops(counts, pw.bs, pw.d)
+    tflops = flops / (us_attn * 1e-6) / 1e12
+    return {"workload": pw.name, "steps": steps, "us_per_prefill": round(us_total, 1),
+            "us_gate": round(us_total - us_attn, 1), "us_attention": round(us_attn, 1),
+            "kept_blocks_per_head": int(counts[0, 0].sum()), "algorithmic_gflop": round(flops / 1e9, 1),
+            "roofline": {"kernel": "prefill_attention_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 def cpu_baseline(w, lay, base_L, plan, args):

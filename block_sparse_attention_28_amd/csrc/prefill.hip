@@ -1,0 +1,446 @@
+// prefill.hip -- SeerAttention block-sparse causal prefill: gate and attention.
+//
+// Operation ("SeerAttention: Learning Intrinsic Sparse Attention in Your
+// LLMs", abstract v1): the gate pools Q and K along the sequence, one vector
+// per bs-token block, projects both through learnable linear layers and
+// multiplies the results into block scores; a block-sparse FlashAttention
+// kernel then attends only the activated blocks.  Here row i of the causal
+// block mask keeps its diagonal block plus the k_i - 1 best earlier blocks,
+// k_i = ceil((i + 1) * keep_num / keep_den) (the 90%-sparsity regime of the
+// v2 abstract at keep 1/10).
+//
+// Kernels (gfx950):
+//   prefill_pool_project : mean-pool Q and K per block (partial last block:
+//                          mean of its rows), project with Wq / Wk (fp32)
+//   prefill_gate_scores  : S_ij = gate_scale * A_i . C_j, fp32 64x64 LDS tiles,
+//                          lower-triangular tiles only
+//   prefill_select_rows  : one wave per row: exact top-(k_i - 1) of j < i with
+//                          lower-id ties, then the diagonal
+//   prefill_attention    : 64 query rows per workgroup (16 per wave), MFMA
+//                          v_mfma_f32_16x16x32_bf16.  S^T = K Q^T so that each
+//                          lane holds one query row's probabilities in exactly
+//                          the operand layout of O^T = V^T P^T; K is staged in
+//                          LDS row-major, V transposed (XOR-swizzled 4-key
+//                          groups); the next kept block's K/V are prefetched
+//                          into registers while the current one is computed.
+#include "seer_device.hpp"
+#include "seer_host.hpp"
+#include "topk_wave.hpp"
+
+#include <math.h>
+
+namespace seer {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPBS = 64;  // prefill block size (query and key blocks)
+
+__device__ __forceinline__ int keep_count(int i, int num, int den) {
+    const int64_t k = ((int64_t)(i + 1) * num + den - 1) / den;
+    return k < 1 ? 1 : (k > i + 1 ? i + 1 : (int)k);
+}
+
+__device__ __forceinline__ void unpack8f(const uint4 w, float *f) {
+    f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
+    f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+}
+
+// ---------------------------------------------------------------- gate ----
+// One workgroup per (chunk of PB blocks, head, batch).  Thread (rg, c) owns the
+// 16-byte column chunk c of rows rg, rg + RG, ...  Output A, C: fp32 [B][H][nb][dg].
+template <int D>
+__global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_t *q, const uint16_t *k, int H,
+                                                                   int L, int nb, const uint16_t *wq,
+                                                                   const uint16_t *wk, int dg, float *A, float *Cm) {
+    constexpr int CH = D / 8, RG = 256 / CH, PB = 8, WB = 8;
+    const int blk0 = blockIdx.x * PB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int c = tid % CH, rg = tid / CH;
+    __shared__ float part[2][RG][D];
+    __shared__ float pooled[2][PB][D];  // [Q/K][block][dim]
+    const int64_t head = ((int64_t)b * H + h) * L * D;
+    const int nblk = nb - blk0 < PB ? nb - blk0 : PB;
+    for (int p = 0; p < nblk; ++p) {
+        const int t0 = (blk0 + p) * kPBS;
+        const int rows = L - t0 < kPBS ? L - t0 : kPBS;
+        float aq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        uint4 wqv[kPBS / RG], wkv[kPBS / RG];
+#pragma unroll
+        for (int i = 0; i < kPBS / RG; ++i) {
+            const int r = rg + i * RG;
+            const int64_t off = head + (int64_t)(t0 + r) * D + c * 8;
+            wqv[i] = r < rows ? *reinterpret_cast<const uint4 *>(q + off) : make_uint4(0, 0, 0, 0);
+            wkv[i] = r < rows ? *reinterpret_cast<const uint4 *>(k + off) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kPBS / RG; ++i) {
+            float f[8];
+            unpack8f(wqv[i], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aq[e] += f[e];
+            unpack8f(wkv[i], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ak[e] += f[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            part[0][rg][c * 8 + e] = aq[e];
+            part[1][rg][c * 8 + e] = ak[e];
+        }
+        __syncthreads();
+        if (tid < 2 * D) {
+            const int which = tid / D, e = tid % D;
+            float s = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) s += part[which][r][e];
+            pooled[which][p][e] = s / (float)rows;
+        }
+        __syncthreads();
+    }
+    // A[p][r] = Wq[h][r] . qbar_p ; C[p][r] = Wk[h][r] . kbar_p
+    const uint16_t *wqh = wq + (int64_t)h * dg * D + c * 8;
+    const uint16_t *wkh = wk + (int64_t)h * dg * D + c * 8;
+    float *Ah = A + (((int64_t)b * H + h) * nb + blk0) * dg;
+    float *Ch = Cm + (((int64_t)b * H + h) * nb + blk0) * dg;
+    for (int r0 = 0; r0 < dg; r0 += WB * RG) {
+        uint4 w1[WB], w2[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+            const int r = r0 + rg + i * RG;
+            w1[i] = r < dg ? *reinterpret_cast<const uint4 *>(wqh + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
+            w2[i] = r < dg ? *reinterpret_cast<const uint4 *>(wkh + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < WB; ++i) {
+            const int r = r0 + rg + i * RG;
+            float f1[8], f2[8];
+            unpack8f(w1[i], f1);
+            unpack8f(w2[i], f2);
+            for (int p = 0; p < nblk; ++p) {
+                float sa = 0.f, sc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sa = fmaf(f1[e], pooled[0][p][c * 8 + e], sa);
+                    sc = fmaf(f2[e], pooled[1][p][c * 8 + e], sc);
+                }
+                sa = group_sum<CH>(sa);
+                sc = group_sum<CH>(sc);
+                if (c == 0 && r < dg) {
+                    Ah[(int64_t)p * dg + r] = sa;
+                    Ch[(int64_t)p * dg + r] = sc;
+                }
+            }
+        }
+    }
+}
+
+// S[b][h][i][j] = gate_scale * A_i . C_j for the lower-triangular 64x64 tiles.
+// One workgroup per (row tile, column tile <= row tile, head*batch).
+__global__ __launch_bounds__(256) void prefill_gate_scores_kernel(const float *A, const float *Cm, int nb, int dg,
+                                                                  float gate_scale, float *S) {
+    constexpr int T = 64, KC = 32;
+    const int it = blockIdx.x, jt = blockIdx.y, bh = blockIdx.z;
+    if (jt > it) return;
+    __shared__ float as[KC][T + 1], cs[KC][T + 1];
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const float *Ab = A + (int64_t)bh * nb * dg, *Cb = Cm + (int64_t)bh * nb * dg;
+    float acc[4][4] = {};
+    for (int e0 = 0; e0 < dg; e0 += KC) {
+        for (int x = tid; x < T * KC; x += 256) {
+            const int r = x / KC, e = x % KC;
+            const int ri = it * T + r, rj = jt * T + r;
+            as[e][r] = (ri < nb && e0 + e < dg) ? Ab[(int64_t)ri * dg + e0 + e] : 0.f;
+            cs[e][r] = (rj < nb && e0 + e < dg) ? Cb[(int64_t)rj * dg + e0 + e] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int e = 0; e < KC; ++e) {
+            float a[4], cc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = as[e][ty * 4 + u];
+                cc[u] = cs[e][tx * 4 + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], cc[v], acc[u][v]);
+        }
+        __syncthreads();
+    }
+    float *Sb = S + (int64_t)bh * nb * nb;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = it * T + ty * 4 + u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int j = jt * T + tx * 4 + v;
+            if (i < nb && j < nb && j <= i) Sb[(int64_t)i * nb + j] = acc[u][v] * gate_scale;
+        }
+    }
+}
+
+// Row i keeps the best k_i - 1 blocks j < i (lower id on ties), ascending, then i.
+__global__ __launch_bounds__(256) void prefill_select_rows_kernel(const float *S, int BH, int nb, int slice,
+                                                                  int keep_num, int keep_den, int kmax_row,
+                                                                  int32_t *kv_blocks, int32_t *kv_count) {
+    extern __shared__ uint32_t lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;  // bh * nb + i
+    if (row >= (int64_t)BH * nb) return;
+    const int i = (int)(row % nb);
+    uint32_t *keys = lds + (size_t)wave * slice;
+    int *hist = reinterpret_cast<int *>(keys + slice - 256);
+    int32_t *out = kv_blocks + row * kmax_row;
+    int ki = keep_count(i, keep_num, keep_den);
+    ki = ki > kmax_row ? kmax_row : ki;
+    const int need = ki - 1;
+    if (need > 0 && need < i) {
+        wave_topk_ascending(S + row * nb, i, need, keys, hist, out, lane);
+    } else if (need > 0) {  // every earlier block is kept
+        for (int m = lane; m < need; m += 64) out[m] = m;
+    }
+    wave_lds_sync();
+    for (int m = need + lane; m < kmax_row; m += 64) out[m] = m == need ? i : -1;
+    if (lane == 0) kv_count[row] = need + 1;
+}
+
+// ----------------------------------------------------------- attention ----
+__device__ __forceinline__ int vt_index(int d, int key) {  // V^T[d][key], 4-key groups XOR-swizzled by row
+    const int swz = (d ^ (d >> 3)) & 15;
+    return d * kPBS + ((((key >> 2) ^ swz) & 15) << 2) + (key & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_t *q, const uint16_t *k,
+                                                                   const uint16_t *v, int H, int L, int nb,
+                                                                   const int32_t *kv_blocks,
+                                                                   const int32_t *kv_count, int kmax_row,
+                                                                   float scale_log2, uint16_t *out, float *lse) {
+    constexpr int KS = D / 32;           // k-steps of S^T = K Q^T
+    constexpr int DT = D / 16;           // 16-wide d tiles of O^T
+    constexpr int KPAD = D + 8;          // K row stride in LDS (elements)
+    constexpr int CPR = D / 8;           // 16-byte chunks per row
+    constexpr int KCH = kPBS * CPR / 256;        // K chunks per thread
+    constexpr int VPR = (kPBS / 2) * CPR / 256;  // V row-pair chunks per thread
+    __shared__ __align__(16) uint16_t k_lds[kPBS * KPAD];
+    __shared__ __align__(16) uint16_t vt_lds[D * kPBS];
+
+    // Longest rows first: within each (b, h) the last query block comes first.
+    const int64_t wi = blockIdx.x;
+    const int64_t per_b = (int64_t)H * nb;
+    const int b = (int)(wi / per_b);
+    const int rem = (int)(wi % per_b);
+    const int h = rem / nb;
+    const int i = nb - 1 - rem % nb;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t head = ((int64_t)b * H + h) * L * D;
+    const uint16_t *qh = q + head, *kh = k + head, *vh = v + head;
+    const int qtok = i * kPBS + wave * 16 + n;  // this lane's query row
+
+    bf16x8_t qop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 w = qtok < L ? *reinterpret_cast<const uint4 *>(qh + (int64_t)qtok * D + 8 * g + 32 * ks)
+                           : make_uint4(0, 0, 0, 0);
+        qop[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    f32x4_t oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int64_t row = ((int64_t)b * H + h) * nb + i;
+    int cnt = kv_count[row];
+    cnt = cnt < 0 ? 0 : (cnt > kmax_row ? kmax_row : cnt);
+    const int32_t *blist = kv_blocks + row * kmax_row;
+
+    uint4 kreg[KCH], vreg[VPR][2];
+    auto fetch = [&](int it) {
+        int j = blist[it];
+        j = j < 0 ? 0 : (j > i ? i : j);
+        const int k0 = j * kPBS;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
+            const int tok = k0 + r;
+            kreg[c] = tok < L ? *reinterpret_cast<const uint4 *>(kh + (int64_t)tok * D + cc * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < VPR; ++c) {
+            const int item = tid + 256 * c, rp = item / CPR, cc = item % CPR;
+            const int tok = k0 + 2 * rp;
+            vreg[c][0] = tok < L ? *reinterpret_cast<const uint4 *>(vh + (int64_t)tok * D + cc * 8) : make_uint4(0, 0, 0, 0);
+            vreg[c][1] = tok + 1 < L ? *reinterpret_cast<const uint4 *>(vh + (int64_t)(tok + 1) * D + cc * 8)
+                                     : make_uint4(0, 0, 0, 0);
+        }
+    };
+    if (cnt > 0) fetch(0);
+
+    for (int it = 0; it < cnt; ++it) {
+        int j = blist[it];
+        j = j < 0 ? 0 : (j > i ? i : j);
+        const int k0 = j * kPBS;
+        __syncthreads();  // previous block's LDS reads are done
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
+            *reinterpret_cast<uint4 *>(&k_lds[r * KPAD + cc * 8]) = kreg[c];
+        }
+#pragma unroll
+        for (int c = 0; c < VPR; ++c) {
+            const int item = tid + 256 * c, rp = item / CPR, cc = item % CPR;
+            const uint32_t a4[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
+            const uint32_t b4[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t lo = (a4[e2] & 0xffffu) | (b4[e2] << 16);           // column 2*e2
+                const uint32_t hi = (a4[e2] >> 16) | (b4[e2] & 0xffff0000u);       // column 2*e2+1
+                *reinterpret_cast<uint32_t *>(&vt_lds[vt_index(cc * 8 + 2 * e2, 2 * rp)]) = lo;
+                *reinterpret_cast<uint32_t *>(&vt_lds[vt_index(cc * 8 + 2 * e2 + 1, 2 * rp)]) = hi;
+            }
+        }
+        __syncthreads();
+        if (it + 1 < cnt) fetch(it + 1);  // in flight while this block is computed
+
+        // S^T[key][qrow] for the 64 keys of block j, 16 at a time.
+        f32x4_t s[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&k_lds[(16 * t + n) * KPAD + 8 * g + 32 * ks]);
+                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], s[t], 0, 0, 0);
+            }
+        }
+        // Lane holds keys 16t + 4g + e of query row qtok; causal + length masks.
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ktok = k0 + 16 * t + 4 * g + e;
+                float x = s[t][e] * scale_log2;
+                x = (ktok > qtok || ktok >= L) ? -INFINITY : x;
+                s[t][e] = x;
+                mloc = fmax_fast(mloc, x);
+            }
+        mloc = max_xor32(max_xor16(mloc));  // the 4 lanes of this query row
+        const float m_new = fmax_fast(m_run, mloc);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_ref);
+        m_run = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = fast_exp2(s[t][e] - m_ref);
+                s[t][e] = p;
+                lsum += p;
+            }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        // P^T operand: k-slots 8g..8g+3 <- keys 32ks + 4g + e, 8g+4..8g+7 <- keys 32ks + 16 + 4g + e.
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pb[ks][e] = (__bf16)s[2 * ks][e];
+                pb[ks][4 + e] = (__bf16)s[2 * ks + 1][e];
+            }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int dcol = 16 * dt + n;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint2 lo = *reinterpret_cast<const uint2 *>(&vt_lds[vt_index(dcol, 32 * ks + 4 * g)]);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(&vt_lds[vt_index(dcol, 32 * ks + 16 + 4 * g)]);
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], oacc[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    const float l_tot = sum_xor32(sum_xor16(l_run));
+    if (qtok < L) {
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        uint16_t *orow = out + head + (int64_t)qtok * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint32_t w0 = (uint32_t)f32_to_bf16(oacc[dt][0] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][1] * inv) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16(oacc[dt][2] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = make_uint2(w0, w1);
+        }
+        if (g == 0 && lse) lse[((int64_t)b * H + h) * L + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+}  // namespace seer
+
+using namespace seer;
+
+static int prefill_kmax_row(int nb, int num, int den) {
+    int64_t k = ((int64_t)nb * num + den - 1) / den;
+    return (int)(k < 1 ? 1 : (k > nb ? nb : k));
+}
+
+extern "C" int seer_block_sparse_prefill_kmax_row(int L, int block_size, int keep_num, int keep_den) {
+    if (L <= 0 || block_size <= 0 || keep_num < 0 || keep_den <= 0) return 0;
+    return prefill_kmax_row((L + block_size - 1) / block_size, keep_num, keep_den);
+}
+
+extern "C" size_t seer_block_sparse_prefill_workspace_size(int B, int H, int L, int d, int block_size, int dg) {
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block_size <= 0 || dg <= 0) return 0;
+    const size_t nb = (size_t)(L + block_size - 1) / block_size;
+    const size_t bh = (size_t)B * H;
+    return (2 * bh * nb * dg + bh * nb * nb) * sizeof(float);
+}
+
+extern "C" int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k, const seer_bf16 *v, int B, int H,
+                                         int L, int d, int block_size, const seer_bf16 *wq, const seer_bf16 *wk,
+                                         int dg, float gate_scale, int keep_num, int keep_den, int32_t *kv_blocks,
+                                         int32_t *kv_count, int kmax_row, int use_given_blocks, float softmax_scale,
+                                         void *workspace, size_t workspace_bytes, seer_bf16 *out, float *lse,
+                                         hipStream_t stream) {
+    if (!q || !k || !v || !kv_blocks || !kv_count || !out) return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || L <= 0 || kmax_row <= 0 || !(softmax_scale == softmax_scale)) return SEER_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SEER_ERR_INVALID_ARG;
+    if (d != 128 || block_size != kPBS) return SEER_ERR_UNSUPPORTED;
+    const int nb = (L + kPBS - 1) / kPBS;
+    const int64_t rows = (int64_t)B * H * nb;
+    if (rows > 0x7fffffffLL || (int64_t)B * H > 65535) return SEER_ERR_INVALID_ARG;
+    if (!use_given_blocks) {
+        if (!wq || !wk || dg < 1 || dg > 256 || keep_num < 0 || keep_den <= 0 || !(gate_scale == gate_scale) ||
+            !aligned16(wq) || !aligned16(wk))
+            return SEER_ERR_INVALID_ARG;
+        if (kmax_row < prefill_kmax_row(nb, keep_num, keep_den)) return SEER_ERR_INVALID_ARG;
+        if (nb > 16384 - 256) return SEER_ERR_UNSUPPORTED;
+        const size_t need = seer_block_sparse_prefill_workspace_size(B, H, L, d, kPBS, dg);
+        if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SEER_ERR_WORKSPACE;
+        float *A = static_cast<float *>(workspace);
+        float *Cm = A + (size_t)B * H * nb * dg;
+        float *S = Cm + (size_t)B * H * nb * dg;
+        prefill_pool_project_kernel<128><<<dim3((nb + 7) / 8, H, B), 256, 0, stream>>>(q, k, H, L, nb, wq, wk, dg, A,
+                                                                                       Cm);
+        int st = launch_status();
+        if (st != SEER_OK) return st;
+        const int nt = (nb + 63) / 64;
+        prefill_gate_scores_kernel<<<dim3(nt, nt, B * H), 256, 0, stream>>>(A, Cm, nb, dg, gate_scale, S);
+        if ((st = launch_status()) != SEER_OK) return st;
+        const int slice = nb + 256;
+        int waves = (int)(65536 / ((size_t)slice * 4));
+        waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+        prefill_select_rows_kernel<<<dim3((unsigned)((rows + waves - 1) / waves)), 64 * waves,
+                                     (size_t)waves * slice * sizeof(uint32_t), stream>>>(
+            S, B * H, nb, slice, keep_num, keep_den, kmax_row, kv_blocks, kv_count);
+        if ((st = launch_status()) != SEER_OK) return st;
+    }
+    prefill_attention_kernel<128><<<dim3((unsigned)rows), 256, 0, stream>>>(
+        q, k, v, H, L, nb, kv_blocks, kv_count, kmax_row, softmax_scale * kLog2e, out, lse);
+    return launch_status();
+}

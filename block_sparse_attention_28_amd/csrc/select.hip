@@ -7,51 +7,15 @@
 // id, and emit the kept ids in ascending order (so decoding reads memory
 // forward).
 //
-// One wavefront per (b, head), several per workgroup, no workgroup barriers.
-// Scores become order-preserving 32-bit keys held in the wave's LDS slice; an
-// 8-bit-digit radix select (four histogram passes from the most significant
-// digit, a wave prefix sum over the 256 bins) finds the k-th largest key T and
-// how many keys equal to T must be taken.  A last sweep over the ids in order
-// keeps keys > T plus the first `need` keys == T, placing each kept id with a
-// ballot + lane-mask popcount, so the output is ascending by construction.
-// All decisions are integer comparisons of the fp32 score bits.
+// One wavefront per (b, head), several per workgroup, no workgroup barriers;
+// the exact radix top-k itself is in topk_wave.hpp.
 #include "seer_device.hpp"
 #include "seer_host.hpp"
+#include "topk_wave.hpp"
 
 namespace seer {
 
 constexpr int kSelMaxBlocks = 16384 - 256;  // keys + histogram of one wave fit in 64 KiB of LDS
-
-__device__ __forceinline__ uint32_t order_key(float s) {
-    uint32_t u = __float_as_uint(s);
-    if (s == 0.0f) u = 0u;  // +0 and -0 compare equal
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inclusive prefix sum over the 64 lanes: DPP row shifts within 16-lane rows,
-// then row broadcasts of lanes 15 and 31 into the following rows.
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-    (void)lane;
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
-    return v;
-}
-
-// Number of lanes below this one whose bit is set in `mask`.
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// Order LDS accesses of this wave (executed in issue order by the hardware).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __global__ __launch_bounds__(256) void select_blocks_kernel(const float *scores, const int32_t *seqlens, int B,
                                                             int H, int nb_max, int slice, int block_size, int k_max,
@@ -75,79 +39,7 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(const float *scores,
         for (int i = lane; i < k_max; i += 64) out[i] = i < k ? i : -1;
         return;
     }
-    const float *sc = scores + (int64_t)pair * nb_max;
-    for (int base = 0; base < nc; base += 64 * 8) {  // eight loads in flight per lane
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = base + lane + 64 * i;
-            v[i] = j < nc ? sc[j] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = base + lane + 64 * i;
-            if (j < nc) keys[j] = order_key(v[i]);
-        }
-    }
-
-    uint32_t prefix = 0;
-    int need = k;  // keys still to take among those matching `prefix` so far
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hist[lane * 4 + i] = 0;
-        wave_lds_sync();
-        for (int j = lane; j < nc; j += 64) {
-            const uint32_t key = keys[j];
-            if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-        }
-        wave_lds_sync();
-        // lane l covers digits 255-4l .. 252-4l, in descending order
-        int cnt[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - 4 * lane - i];
-        const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-        const int incl = wave_inclusive_scan(local, lane);
-        const int excl = incl - local;
-        const uint64_t hit = __ballot(excl < need && incl >= need);
-        int src = __ffsll((long long)hit) - 1;
-        src = src < 0 ? 0 : src;
-        int digit = 0, rest = 0;
-        if (lane == src) {
-            int cum = excl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (cum + cnt[i] >= need) {
-                    digit = 255 - 4 * lane - i;
-                    rest = need - cum;
-                    break;
-                }
-                cum += cnt[i];
-            }
-        }
-        digit = __builtin_amdgcn_readlane(digit, src);
-        need = __builtin_amdgcn_readlane(rest, src);
-        prefix |= (uint32_t)digit << shift;
-        wave_lds_sync();
-    }
-    const uint32_t T = prefix;
-
-    // Ids in ascending order, 64 per round: keep key > T, and the first `need` keys == T.
-    int written = 0, eq_seen = 0;
-    for (int base = 0; base < nc; base += 64) {
-        const int j = base + lane;
-        const uint32_t key = j < nc ? keys[j] : 0u;
-        const bool eq = j < nc && key == T;
-        const uint64_t eq_mask = __ballot(eq);
-        const bool take = j < nc && (key > T || (eq && eq_seen + lanes_below(eq_mask) < need));
-        const uint64_t take_mask = __ballot(take);
-        const int pos = written + lanes_below(take_mask);
-        if (take && pos < k) out[pos] = j;
-        written += __popcll(take_mask);
-        eq_seen += __popcll(eq_mask);
-    }
+    wave_topk_ascending(scores + (int64_t)pair * nb_max, nc, k, keys, hist, out, lane);
     for (int i = k + lane; i < k_max; i += 64) out[i] = -1;
 }
 

@@ -1,0 +1,123 @@
+// topk_wave.hpp -- exact top-k of fp32 scores by one wavefront (device helpers).
+//
+// Scores become order-preserving 32-bit keys in LDS; an 8-bit-digit radix
+// select (four histogram passes from the most significant digit, a DPP prefix
+// sum over the 256 bins) finds the k-th largest key T and how many keys equal
+// to T must be taken; a last sweep over the ids in order keeps keys > T plus
+// the first `need` keys == T, placing each with a ballot + lane-mask popcount.
+// The result is the k largest scores, equal scores ordered by the lower id,
+// emitted in ascending id order.
+#pragma once
+
+#include "seer_device.hpp"
+
+namespace seer {
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (s == 0.0f) u = 0u;  // +0 and -0 compare equal
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts within 16-lane rows,
+// then row broadcasts of lanes 15 and 31 into the following rows.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+    (void)lane;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Order LDS accesses of this wave (executed in issue order by the hardware).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Select the k largest of scores[0..n) (0 < k < n), write their ids ascending to
+// out[0..k).  keys: LDS scratch of n words, hist: LDS scratch of 256 words, both
+// private to this wave.  Every lane of the wave must call it.
+__device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, int k, uint32_t *keys, int *hist,
+                                                    int32_t *out, int lane) {
+    for (int base = 0; base < n; base += 64 * 8) {  // eight loads in flight per lane
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = base + lane + 64 * i;
+            v[i] = j < n ? scores[j] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = base + lane + 64 * i;
+            if (j < n) keys[j] = order_key(v[i]);
+        }
+    }
+    uint32_t prefix = 0;
+    int need = k;  // keys still to take among those matching `prefix` so far
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hist[lane * 4 + i] = 0;
+        wave_lds_sync();
+        for (int j = lane; j < n; j += 64) {
+            const uint32_t key = keys[j];
+            if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        wave_lds_sync();
+        // lane l covers digits 255-4l .. 252-4l, in descending order
+        int cnt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - 4 * lane - i];
+        const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+        const int incl = wave_inclusive_scan(local, lane);
+        const int excl = incl - local;
+        const uint64_t hit = __ballot(excl < need && incl >= need);
+        int src = __ffsll((long long)hit) - 1;
+        src = src < 0 ? 0 : src;
+        int digit = 0, rest = 0;
+        if (lane == src) {
+            int cum = excl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (cum + cnt[i] >= need) {
+                    digit = 255 - 4 * lane - i;
+                    rest = need - cum;
+                    break;
+                }
+                cum += cnt[i];
+            }
+        }
+        digit = __builtin_amdgcn_readlane(digit, src);
+        need = __builtin_amdgcn_readlane(rest, src);
+        prefix |= (uint32_t)digit << shift;
+        wave_lds_sync();
+    }
+    const uint32_t T = prefix;
+    int written = 0, eq_seen = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int j = base + lane;
+        const uint32_t key = j < n ? keys[j] : 0u;
+        const bool eq = j < n && key == T;
+        const uint64_t eq_mask = __ballot(eq);
+        const bool take = j < n && (key > T || (eq && eq_seen + lanes_below(eq_mask) < need));
+        const uint64_t take_mask = __ballot(take);
+        const int pos = written + lanes_below(take_mask);
+        if (take && pos < k) out[pos] = j;
+        written += __popcll(take_mask);
+        eq_seen += __popcll(eq_mask);
+    }
+}
+
+}  // namespace seer

@@ -33,6 +33,10 @@ SIGNATURES = {
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
+    "seer_block_sparse_prefill_kmax_row": (_I, [_I, _I, _I, _I]),
+    "seer_block_sparse_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "seer_block_sparse_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _F, _I, _I, _P, _P, _I, _I, _F,
+                                       _P, _SZ, _P, _P, _P]),
 }
 
 
@@ -143,3 +147,27 @@ def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, soft
           k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
           block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
           _ptr(lse), _stream(stream))
+
+
+def seer_block_sparse_prefill_kmax_row(L: int, block_size: int, keep_num: int, keep_den: int) -> int:
+    return load().seer_block_sparse_prefill_kmax_row(L, block_size, keep_num, keep_den)
+
+
+def seer_block_sparse_prefill_workspace_size(B: int, H: int, L: int, d: int, block_size: int, dg: int) -> int:
+    return load().seer_block_sparse_prefill_workspace_size(B, H, L, d, block_size, dg)
+
+
+def seer_block_sparse_prefill(q, k, v, block_size: int, wq, wk, gate_scale: float, keep_num: int, keep_den: int,
+                              kv_blocks, kv_count, softmax_scale: float, out, lse=None, workspace=None,
+                              use_given_blocks: bool = False, stream=None):
+    """Block-sparse causal prefill of q, k, v [B, H, L, d] bf16 into out; kv_blocks [B, H, nb, kmax_row]."""
+    _bits(q), _bits(k), _bits(v), _bits(out)
+    B, H, L, d = q.shape
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous() and out.is_contiguous()
+    assert kv_blocks.dtype == torch.int32 and kv_count.dtype == torch.int32 and kv_blocks.is_contiguous()
+    dg = wq.shape[1] if wq is not None else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("seer_block_sparse_prefill", _ptr(q), _ptr(k), _ptr(v), B, H, L, d, block_size, _ptr(wq), _ptr(wk), dg,
+          float(gate_scale), keep_num, keep_den, _ptr(kv_blocks), _ptr(kv_count), kv_blocks.shape[-1],
+          1 if use_given_blocks else 0, float(softmax_scale), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+          _stream(stream))

@@ -149,6 +149,46 @@ int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                        float softmax_scale, int num_splits, void *workspace, size_t workspace_bytes,
                        void *out, int out_dtype, float *lse, hipStream_t stream);
 
+/*
+ * Block-sparse causal prefill (SeerAttention, abstract v1: the gate pools Q and
+ * K per block, projects both through learnable linear layers and multiplies
+ * them into block scores; a block-sparse FlashAttention kernel attends only
+ * the activated blocks).  Per (b, h), with nb = ceil(L / block_size) blocks:
+ *
+ *   Qbar_i, Kbar_j   mean of the rows of block i / j (a partial last block:
+ *                    mean of the rows it has)
+ *   S_ij = gate_scale * (Wq[h] Qbar_i) . (Wk[h] Kbar_j)          j <= i
+ *   row i keeps k_i = ceil((i + 1) * keep_num / keep_den) blocks (at least 1,
+ *   at most i + 1): the diagonal block i plus the k_i - 1 best j < i, equal
+ *   scores ordered by the lower id; kv_blocks[b][h][i][0..k_i) lists them in
+ *   ascending order (so the diagonal last), -1 after; kv_count[b][h][i] = k_i.
+ *   out[b][h][t] = softmax attention of query token t (in block i) over the
+ *   tokens t' <= t of row i's kept blocks, scale softmax_scale;
+ *   lse[b][h][t] = log of its softmax denominator (natural log).
+ *
+ * With use_given_blocks != 0 the gate is skipped: kv_blocks / kv_count are
+ * inputs (ids are clamped into [0, i]; counts into [0, kmax_row]; a row with
+ * count 0 gives zeros and lse = -inf) and wq, wk, workspace may be NULL.
+ *   q, k, v, out  bf16 [B][H][L][d], dense
+ *   wq, wk        bf16 [H][dg][d], dense
+ *   kv_blocks     int32 [B][H][nb][kmax_row]; kv_count int32 [B][H][nb]
+ *   lse           fp32 [B][H][L] or NULL
+ *   workspace     >= seer_block_sparse_prefill_workspace_size(...) bytes (fp32
+ *                 projected pooled Q and K and the block score matrix)
+ * d = 128, block_size = 64, 1 <= dg <= 256; without given blocks,
+ * kmax_row >= seer_block_sparse_prefill_kmax_row(L, block_size, keep_num, keep_den)
+ * and nb <= 16128.
+ */
+int seer_block_sparse_prefill_kmax_row(int L, int block_size, int keep_num, int keep_den);
+size_t seer_block_sparse_prefill_workspace_size(int B, int H, int L, int d, int block_size, int dg);
+int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k, const seer_bf16 *v,
+                              int B, int H, int L, int d, int block_size,
+                              const seer_bf16 *wq, const seer_bf16 *wk, int dg, float gate_scale,
+                              int keep_num, int keep_den, int32_t *kv_blocks, int32_t *kv_count,
+                              int kmax_row, int use_given_blocks, float softmax_scale,
+                              void *workspace, size_t workspace_bytes, seer_bf16 *out, float *lse,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
