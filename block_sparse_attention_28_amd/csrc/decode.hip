@@ -11,18 +11,23 @@
 // gfx950 design.  One workgroup (4 waves) per (split, KV head, sequence).  A
 // split owns a contiguous range of "units" (a kept block, or the tail).  For
 // every unit each wave takes a quarter of the block's tokens:
+//   loads : non-temporal 16-byte buffer loads; the unit's first row is a
+//        scalar offset, each lane's rows a fixed 32-bit offset, and rows past
+//        the cache read as zero (the descriptor's range check).
 //   QK : 8 lanes per key row, each lane a 16-byte chunk per 64 head dims;
 //        v_dot2_f32_bf16 with the bf16 query held in registers, then an
 //        8-lane DPP all-reduce.  The key bytes feed all G query heads.
-//   softmax : scores in the log2 domain; one running max per head that is
-//        uniform across the wave, so partial sums need no rescaling when the
-//        wave's lane groups are combined.
+//   softmax : log2 domain, the scale folded into one FMA; one running max
+//        per head that is uniform across the wave, so partial sums need no
+//        rescaling when the wave's lane groups are combined, and the
+//        accumulators are rescaled only when some head's maximum moved.
 //   PV : probabilities go through LDS to a second layout, one 16-byte value
 //        chunk per lane (a whole 256-byte row per 16 lanes, fully coalesced),
 //        fp32 FMA into G x 8 accumulators per lane.
 // At the end the wave's lane groups and then the 4 waves are combined, and
 // the split writes (unnormalised o, running max, running sum) per head -- or,
-// with a single split, the final normalised output directly.
+// with a single split, the final normalised output directly.  A second small
+// kernel merges the splits by log-sum-exp.
 #include "seer_device.hpp"
 #include "seer_host.hpp"
 
@@ -62,6 +67,17 @@ struct DecodeCfg {
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor word 3 for plain 32-bit dword access (gfx9 family).
+constexpr int kBufferFlags = 0x00020000;
+
+// 16-byte non-temporal load at descriptor base + voff + soff (bytes); reads past
+// the descriptor's range return zero.
+__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t t = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ uint4 ldg16_stream(const uint16_t *p) {
     const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
@@ -114,10 +130,23 @@ __global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const Decod
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
     }
 
+    // K/V of (b, g) through buffer descriptors: a unit's first row is a scalar
+    // byte offset, each lane's rows and chunks a fixed 32-bit offset.
     const uint16_t *kb = a.k + b * a.skv_b + g * a.skv_h;
     const uint16_t *vb = a.v + b * a.skv_b + g * a.skv_h;
+    const uint32_t region = (uint32_t)((int64_t)a.kv_capacity * a.skv_t * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, kBufferFlags);
     const int32_t *sel = a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
     const int wt0 = wave * C::TPW;  // first token of this wave inside a unit
+    uint32_t koff[C::TPL][C::CPL], voff[C::TPLV];
+#pragma unroll
+    for (int t = 0; t < C::TPL; ++t)
+#pragma unroll
+        for (int i = 0; i < C::CPL; ++i)
+            koff[t][i] = (uint32_t)(((wt0 + r + t * C::ROWS) * a.skv_t + (c + i * C::LPR) * 8) * 2);
+#pragma unroll
+    for (int t = 0; t < C::TPLV; ++t) voff[t] = (uint32_t)(((wt0 + rv + t * C::ROWSV) * a.skv_t + cv * 8) * 2);
 
     for (int u = u0; u < u1; ++u) {
         int tok0, cnt;
@@ -130,27 +159,23 @@ __global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const Decod
             tok0 = nc * BS;
             cnt = tail;
         }
+        tok0 = __builtin_amdgcn_readfirstlane(tok0);
+        cnt = __builtin_amdgcn_readfirstlane(cnt);
+        // Rows past the end of the cache read as zero (buffer range check) and,
+        // like rows past cnt, are masked out of the softmax.
+        const uint32_t soff = (uint32_t)tok0 * (uint32_t)a.skv_t * 2u;
         uint4 kr[C::TPL][C::CPL], vr[C::TPLV];
 #pragma unroll
-        for (int t = 0; t < C::TPL; ++t) {
-            int tt = wt0 + r + t * C::ROWS;
-            tt = tt < cnt ? tt : cnt - 1;
-            const uint16_t *row = kb + (int64_t)(tok0 + tt) * a.skv_t;
+        for (int t = 0; t < C::TPL; ++t)
 #pragma unroll
-            for (int i = 0; i < C::CPL; ++i) kr[t][i] = ldg16_stream(row + (c + i * C::LPR) * 8);
-        }
+            for (int i = 0; i < C::CPL; ++i) kr[t][i] = buf_ld16_nt(krs, koff[t][i], soff);
 #pragma unroll
-        for (int t = 0; t < C::TPLV; ++t) {
-            int tt = wt0 + rv + t * C::ROWSV;
-            tt = tt < cnt ? tt : cnt - 1;
-            vr[t] = ldg16_stream(vb + (int64_t)(tok0 + tt) * a.skv_t + cv * 8);
-        }
+        for (int t = 0; t < C::TPLV; ++t) vr[t] = buf_ld16_nt(vrs, voff[t], soff);
 
-        // Scores of this lane group's key rows for every head (log2 domain).
+        // Raw scores q.k of this lane group's key rows for every head.
         float s[C::TPL][G];
 #pragma unroll
-        for (int t = 0; t < C::TPL; ++t) {
-            const bool valid = wt0 + r + t * C::ROWS < cnt;
+        for (int t = 0; t < C::TPL; ++t)
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float acc = 0.f;
@@ -161,27 +186,33 @@ __global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const Decod
                     acc = dot2_bf16(qv[h][i].z, kr[t][i].z, acc);
                     acc = dot2_bf16(qv[h][i].w, kr[t][i].w, acc);
                 }
-                acc = group_sum<C::LPR>(acc) * a.scale_log2;
-                s[t][h] = valid ? acc : -INFINITY;
+                s[t][h] = group_sum<C::LPR>(acc);
             }
+        if (cnt < BS) {  // the tail unit: rows past the context take no weight
+#pragma unroll
+            for (int t = 0; t < C::TPL; ++t)
+#pragma unroll
+                for (int h = 0; h < G; ++h) s[t][h] = wt0 + r + t * C::ROWS < cnt ? s[t][h] : -INFINITY;
         }
 
-        // Wave-uniform running max per head, rescale factors, probabilities.
+        // Wave-uniform running max per head (log2 domain), rescale factors, probabilities.
         float alpha[G];
+        bool rescale = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mx = s[0][h];
 #pragma unroll
             for (int t = 1; t < C::TPL; ++t) mx = fmax_fast(mx, s[t][h]);
-            mx = cross_group_max<C::LPR>(mx);
+            mx = cross_group_max<C::LPR>(mx) * a.scale_log2;  // the scale is positive
             const float m_new = fmax_fast(m_run[h], mx);
             const float m_ref = m_new == -INFINITY ? 0.f : m_new;
             alpha[h] = fast_exp2(m_run[h] - m_ref);
+            rescale |= alpha[h] != 1.0f;
             m_run[h] = m_new;
             float lsum = 0.f;
 #pragma unroll
             for (int t = 0; t < C::TPL; ++t) {
-                s[t][h] = fast_exp2(s[t][h] - m_ref);
+                s[t][h] = fast_exp2(fmaf(s[t][h], a.scale_log2, -m_ref));
                 lsum += s[t][h];
             }
             l_part[h] = l_part[h] * alpha[h] + lsum;
@@ -199,10 +230,13 @@ __global__ __launch_bounds__(256, 2) void sparse_decode_split_kernel(const Decod
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+        if (rescale) {  // wave-uniform: the running maxima are the same in every lane
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+                for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+        }
+        // PV in fp32: one 16-byte value chunk per lane, every head's probability from LDS.
 #pragma unroll
         for (int t = 0; t < C::TPLV; ++t) {
             float p[G];
@@ -381,6 +415,7 @@ extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h
     const size_t need = seer_sparse_decode_workspace_size(B, Hq, Hkv, d, k_max, block_size, S);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SEER_ERR_WORKSPACE;
     if (S > kMaxSplits) return SEER_ERR_INVALID_ARG;
+    if ((int64_t)kv_capacity * skv_t * 2 > 0x7fffffffLL) return SEER_ERR_UNSUPPORTED;  // buffer offsets are 32-bit
 
     DecodeArgs a;
     a.q = q; a.sq_b = sq_b; a.sq_h = sq_h;

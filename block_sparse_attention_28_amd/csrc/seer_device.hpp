@@ -50,7 +50,8 @@ __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ float fmax_fast(float a, float b) { return a > b ? a : b; }
+// max(a, b) for non-NaN inputs in one VALU op: the median of (a, b, +inf).
+__device__ __forceinline__ float fmax_fast(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __builtin_inff()); }
 
 // gfx950 permlane swaps exchange 16-lane rows (odd rows of the first operand with
 // even rows of the second) or 32-lane halves.  Fed the same value twice, the two
