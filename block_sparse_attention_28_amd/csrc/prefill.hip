@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void prefill_select_rows_kernel(const float *S
     ki = ki > kmax_row ? kmax_row : ki;
     const int need = ki - 1;
     if (need > 0 && need < i) {
-        wave_topk_ascending(S + row * nb, i, need, keys, hist, out, lane);
+        wave_topk_ascending<LaunchMem>(S + row * nb, i, need, keys, hist, out, lane);
     } else if (need > 0) {  // every earlier block is kept
         for (int m = lane; m < need; m += 64) out[m] = m;
     }

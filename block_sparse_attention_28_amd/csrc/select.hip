@@ -27,20 +27,8 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(const float *scores,
     uint32_t *keys = lds + (size_t)wave * slice;              // [nb_max]
     int *hist = reinterpret_cast<int *>(keys + slice - 256);  // [256]
 
-    const int b = pair / H;
-    int L = seqlens[b];
-    L = L < 0 ? 0 : L;
-    int nc = L / block_size;
-    nc = nc > nb_max ? nb_max : nc;
-    const int k = k_max < nc ? k_max : nc;
-    int32_t *out = block_idx + (int64_t)pair * k_max;
-    if (lane == 0) n_sel[pair] = k;
-    if (k == nc || k == 0) {  // every complete block, or none, is kept
-        for (int i = lane; i < k_max; i += 64) out[i] = i < k ? i : -1;
-        return;
-    }
-    wave_topk_ascending(scores + (int64_t)pair * nb_max, nc, k, keys, hist, out, lane);
-    for (int i = k + lane; i < k_max; i += 64) out[i] = -1;
+    select_pair_item<LaunchMem>(scores, seqlens, H, nb_max, block_size, k_max, block_idx, n_sel, pair, keys, hist,
+                                lane);
 }
 
 }  // namespace seer

@@ -1,0 +1,234 @@
+// step.hip -- one gated sparse decode step in a single persistent launch.
+//
+// The same work as seer_gate_scores + seer_select_blocks + seer_sparse_decode
+// (gate chunks, per-(b, KV head) selection, decode splits, log-sum-exp merges;
+// see gate_items.hpp, topk_wave.hpp and decode_items.hpp for the operation),
+// but run by one grid of resident workgroups: workgroup w takes work items
+// w, w + grid, w + 2 grid, ... in increasing order.  Items are numbered in
+// dependency order -- all gate chunks, then the selections (one per pair),
+// then the decode splits pair by pair, then the merges -- so an item only ever
+// waits for items with smaller numbers: the smallest unfinished item always has
+// its inputs ready, hence no deadlock while the whole grid is resident (the
+// grid is sized from the occupancy of this kernel), and a pair's selection or
+// decode starts as soon as its own inputs are ready instead of after a kernel
+// boundary.
+//
+// Hand-offs between workgroups (scores, kept ids and counts, split partials)
+// use device-coherent loads and stores (the workgroups may sit on different
+// XCDs with separate L2s); a producer waits for its stores to complete before
+// bumping the item's counter, a consumer polls that counter.  Every poll loop
+// has a limit and a shared abort word, so a launch always terminates; the last
+// workgroup out clears the counters for the next launch.
+#include "decode_items.hpp"
+#include "gate_items.hpp"
+#include "seer_host.hpp"
+#include "topk_wave.hpp"
+
+#include <hip/hip_runtime.h>
+
+namespace seer {
+
+// Control words at the head of the workspace.
+enum : int { kCtlFinished = 1, kCtlStatus = 2, kCtlWords = 4 };
+constexpr int kSpinLimit = 1 << 22;
+
+struct StepArgs {
+    GateArgs gate;
+    DecodeArgs dec;
+    int pairs;        // B * Hkv
+    int chunks;       // gate chunks per pair
+    int k_max;
+    int *ctl;         // [kCtlWords + 3 * pairs]
+    int n_gate, n_select, n_decode, total;
+};
+
+__device__ __forceinline__ int ld_dev(int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Wave 0 polls until *ctr >= target (or the launch was aborted); then the
+// workgroup proceeds.  Every decision is made on wave-uniform values so that
+// the compiler keeps the workgroup's control flow uniform around the barriers.
+__device__ __forceinline__ void wait_for(int *ctr, int target, int *status) {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
+        for (int spins = 0;; ++spins) {
+            if (__builtin_amdgcn_readfirstlane(ld_dev(ctr)) >= target) break;
+            if (__builtin_amdgcn_readfirstlane(ld_dev(status)) != 0) break;
+            if (spins >= kSpinLimit) {
+                __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+}
+
+// Every thread's device-coherent stores of this item have completed; then one increment.
+__device__ __forceinline__ void signal_done(int *ctr) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int BS, int G>
+union StepSmem {
+    DecodeSmem<D, BS, G> dec;
+    GateSmem<D> gate;
+    MergeSmem merge;
+};
+
+template <int D, int BS, int G>
+__global__ __launch_bounds__(256, 2) void decode_step_kernel(const StepArgs s) {
+    __shared__ StepSmem<D, BS, G> sm;
+    extern __shared__ uint32_t sel_lds[];  // selection keys [nb_max] + histogram [256], used by wave 0
+    int *ctl = s.ctl;
+    int *gate_done = ctl + kCtlWords, *sel_done = gate_done + s.pairs, *dec_done = sel_done + s.pairs;
+    int *status = ctl + kCtlStatus;
+    const int S = s.dec.num_splits, Hkv = s.dec.Hkv;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int item = blockIdx.x; item < s.total; item += gridDim.x) {
+        __syncthreads();  // the previous item's LDS use is over
+        if (item < s.n_gate) {
+            const int pair = item / s.chunks, chunk = item % s.chunks;
+            gate_chunk_item<D, DeviceMem>(s.gate, chunk, pair, sm.gate);
+            signal_done(gate_done + pair);
+        } else if (item < s.n_gate + s.n_select) {
+            const int pair = item - s.n_gate;
+            wait_for(gate_done + pair, s.chunks, status);
+            if (wave == 0)
+                select_pair_item<DeviceMem>(s.gate.scores, s.gate.seqlens, Hkv, s.gate.nb_max, s.gate.block_size,
+                                            s.k_max, const_cast<int32_t *>(s.dec.block_idx),
+                                            const_cast<int32_t *>(s.dec.n_sel), pair, sel_lds,
+                                            reinterpret_cast<int *>(sel_lds + s.gate.nb_max), threadIdx.x);
+            signal_done(sel_done + pair);
+        } else if (item < s.n_gate + s.n_select + s.n_decode) {
+            const int idx = item - s.n_gate - s.n_select, pair = idx / S, split = idx % S;
+            wait_for(sel_done + pair, 1, status);
+            decode_split_item<D, BS, G, DeviceMem>(s.dec, split, pair % Hkv, pair / Hkv, sm.dec);
+            if (S > 1) signal_done(dec_done + pair);
+        } else {
+            const int pair = item - s.n_gate - s.n_select - s.n_decode;
+            wait_for(dec_done + pair, S, status);
+            const int b = pair / Hkv, g = pair % Hkv;
+            for (int h = 0; h < G; ++h)
+                decode_merge_row<D, DeviceMem>(s.dec.part_o, s.dec.part_ml, S, (int64_t)b * s.dec.Hq + g * G + h,
+                                               s.dec.out, s.dec.out_dtype, s.dec.lse, sm.merge);
+        }
+    }
+    // The last workgroup out clears the counters (not the status word) for the next launch.
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(ctl + kCtlFinished, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (int)gridDim.x - 1;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_last)) {
+        for (int i = threadIdx.x; i < 3 * s.pairs; i += blockDim.x)
+            __hip_atomic_store(gate_done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(ctl + kCtlFinished, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int D, int BS, int G>
+static int launch_step(const StepArgs &s, size_t sel_lds_bytes, hipStream_t stream) {
+    auto kernel = decode_step_kernel<D, BS, G>;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, sel_lds_bytes) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    int grid = device_cu_count() * per_cu;
+    grid = grid < s.total ? grid : s.total;
+    grid = grid < 1 ? 1 : grid;
+    kernel<<<dim3(grid), 256, sel_lds_bytes, stream>>>(s);
+    return launch_status();
+}
+
+template <int D, int BS>
+static int step_dispatch_group(const StepArgs &s, size_t lds, int G, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_step<D, BS, 1>(s, lds, stream);
+        case 2: return launch_step<D, BS, 2>(s, lds, stream);
+        case 4: return launch_step<D, BS, 4>(s, lds, stream);
+        case 8: return launch_step<D, BS, 8>(s, lds, stream);
+    }
+    return SEER_ERR_UNSUPPORTED;
+}
+
+static size_t step_ctl_bytes(int pairs) { return ((size_t)(kCtlWords + 3 * pairs) * sizeof(int) + 255) / 256 * 256; }
+
+}  // namespace seer
+
+using namespace seer;
+
+extern "C" size_t seer_decode_step_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
+                                                  int num_splits) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+    return step_ctl_bytes(B * Hkv) + seer_sparse_decode_workspace_size(B, Hq, Hkv, d, k_max, block_size, num_splits);
+}
+
+extern "C" int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
+                                const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t, int kv_capacity,
+                                const int32_t *seqlens, const seer_bf16 *wq, const seer_bf16 *wk, int dg,
+                                float gate_scale, const float *kpool, int nb_max, int B, int Hq, int Hkv, int d,
+                                int block_size, int budget_tokens, float softmax_scale, int num_splits, float *scores,
+                                int32_t *block_idx, int32_t *n_sel, void *workspace, size_t workspace_bytes,
+                                void *out, int out_dtype, float *lse, hipStream_t stream) {
+    // Host-side checks: the union of the three calls this step replaces.
+    if (!q || !k || !v || !seqlens || !wq || !wk || !kpool || !scores || !n_sel || !out || !workspace)
+        return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || nb_max <= 0 || budget_tokens < 0 || kv_capacity < 0 ||
+        num_splits < 0 || dg < 1 || dg > 256 || !(gate_scale == gate_scale) || !(softmax_scale == softmax_scale))
+        return SEER_ERR_INVALID_ARG;
+    const int k_max = block_size > 0 ? budget_tokens / block_size : 0;
+    if (k_max > 0 && !block_idx) return SEER_ERR_INVALID_ARG;
+    if (out_dtype != SEER_OUT_BF16 && out_dtype != SEER_OUT_F32) return SEER_ERR_INVALID_ARG;
+    if (skv_t < d || !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !rows_aligned16(k, skv_t) ||
+        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !aligned16(wq) || !aligned16(wk) || !aligned16(kpool) ||
+        !aligned16(workspace))
+        return SEER_ERR_INVALID_ARG;
+    const int G = Hq / Hkv;
+    if ((d != 64 && d != 128) || (block_size != 64 && block_size != 128) || !pow2_group(G) || G > 8)
+        return SEER_ERR_UNSUPPORTED;
+    if ((int64_t)kv_capacity * skv_t * 2 > 0x7fffffffLL || nb_max > 16384 - 256) return SEER_ERR_UNSUPPORTED;
+    const int pairs = B * Hkv;
+    const int S = seer_sparse_decode_num_splits(B, Hkv, k_max, block_size, num_splits);
+    if (S > 128 || (int64_t)pairs * (S + 8) > 0x7fffffff / 8) return SEER_ERR_INVALID_ARG;
+    if (workspace_bytes < seer_decode_step_workspace_size(B, Hq, Hkv, d, k_max, block_size, S))
+        return SEER_ERR_WORKSPACE;
+
+    StepArgs s;
+    const int rpb = d == 128 ? GateCfg<128>::RPB : GateCfg<64>::RPB;
+    s.gate = GateArgs{q, sq_b, sq_h, wq, wk, dg, G, Hkv, gate_scale, kpool, nb_max, seqlens, block_size, scores};
+    char *ws = static_cast<char *>(workspace);
+    DecodeArgs &a = s.dec;
+    a.q = q; a.sq_b = sq_b; a.sq_h = sq_h;
+    a.k = k; a.v = v; a.skv_b = skv_b; a.skv_h = skv_h; a.skv_t = skv_t;
+    a.kv_capacity = kv_capacity;
+    a.seqlens = seqlens; a.block_idx = block_idx; a.n_sel = n_sel;
+    a.k_max = k_max; a.Hq = Hq; a.Hkv = Hkv; a.num_splits = S;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.part_o = S > 1 ? reinterpret_cast<float *>(ws + step_ctl_bytes(pairs)) : nullptr;
+    a.part_ml = S > 1 ? reinterpret_cast<float2 *>(a.part_o + (size_t)B * Hq * S * d) : nullptr;
+    a.out = out; a.out_dtype = out_dtype; a.lse = lse;
+    s.pairs = pairs;
+    s.chunks = (nb_max + rpb - 1) / rpb;
+    s.k_max = k_max;
+    s.ctl = reinterpret_cast<int *>(ws);
+    s.n_gate = pairs * s.chunks;
+    s.n_select = pairs;
+    s.n_decode = pairs * S;
+    s.total = s.n_gate + s.n_select + s.n_decode + (S > 1 ? pairs : 0);
+    const size_t lds = ((size_t)nb_max + 256) * sizeof(uint32_t);
+    if (d == 128)
+        return block_size == 128 ? step_dispatch_group<128, 128>(s, lds, G, stream)
+                                 : step_dispatch_group<128, 64>(s, lds, G, stream);
+    return block_size == 128 ? step_dispatch_group<64, 128>(s, lds, G, stream)
+                             : step_dispatch_group<64, 64>(s, lds, G, stream);
+}
+
+extern "C" int seer_decode_step_status(const void *workspace, int *status, hipStream_t stream) {
+    if (!workspace || !status) return SEER_ERR_INVALID_ARG;
+    if (hipMemcpyAsync(status, static_cast<const int *>(workspace) + kCtlStatus, sizeof(int), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SEER_ERR_LAUNCH;
+    return SEER_OK;
+}

@@ -45,8 +45,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Select the k largest of scores[0..n) (0 < k < n), write their ids ascending to
-// out[0..k).  keys: LDS scratch of n words, hist: LDS scratch of 256 words, both
-// private to this wave.  Every lane of the wave must call it.
+// out[0..k); scores are read and ids written through Mem.  keys: LDS scratch of
+// n words, hist: LDS scratch of 256 words, both private to this wave.  Every
+// lane of the wave must call it.
+template <class Mem>
 __device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, int k, uint32_t *keys, int *hist,
                                                     int32_t *out, int lane) {
     for (int base = 0; base < n; base += 64 * 8) {  // eight loads in flight per lane
@@ -54,7 +56,7 @@ __device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int j = base + lane + 64 * i;
-            v[i] = j < n ? scores[j] : 0.f;
+            v[i] = j < n ? Mem::ldf(scores + j) : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -114,10 +116,33 @@ __device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, 
         const bool take = j < n && (key > T || (eq && eq_seen + lanes_below(eq_mask) < need));
         const uint64_t take_mask = __ballot(take);
         const int pos = written + lanes_below(take_mask);
-        if (take && pos < k) out[pos] = j;
+        if (take && pos < k) Mem::sti(out + pos, j);
         written += __popcll(take_mask);
         eq_seen += __popcll(eq_mask);
     }
+}
+
+// Token-budget selection of one (b, head) = pair by one wave: k = min(k_max, nc)
+// blocks (ties to the lower id), ascending in block_idx[pair][0..k), -1 after,
+// and n_sel[pair] = k.
+template <class Mem>
+__device__ __forceinline__ void select_pair_item(const float *scores, const int32_t *seqlens, int H, int nb_max,
+                                                 int block_size, int k_max, int32_t *block_idx, int32_t *n_sel,
+                                                 int pair, uint32_t *keys, int *hist, int lane) {
+    const int b = pair / H;
+    int L = seqlens[b];
+    L = L < 0 ? 0 : L;
+    int nc = L / block_size;
+    nc = nc > nb_max ? nb_max : nc;
+    const int k = k_max < nc ? k_max : nc;
+    int32_t *out = block_idx + (int64_t)pair * k_max;
+    if (k == nc || k == 0) {  // every complete block, or none, is kept
+        for (int i = lane; i < k_max; i += 64) Mem::sti(out + i, i < k ? i : -1);
+    } else {
+        wave_topk_ascending<Mem>(scores + (int64_t)pair * nb_max, nc, k, keys, hist, out, lane);
+        for (int i = k + lane; i < k_max; i += 64) Mem::sti(out + i, -1);
+    }
+    if (lane == 0) Mem::sti(n_sel + pair, k);
 }
 
 }  // namespace seer

@@ -47,6 +47,9 @@ class DecodePlan:
         self.num_splits = seer.seer_sparse_decode_num_splits(s.B, s.Hkv, s.k_max, s.bs, num_splits)
         dws = seer.seer_sparse_decode_workspace_size(s.B, s.Hq, s.Hkv, s.d, s.k_max, s.bs, self.num_splits)
         self.decode_ws = torch.empty((max(dws, 16) + 3) // 4, dtype=torch.float32, device=dev)
+        sws = seer.seer_decode_step_workspace_size(s.B, s.Hq, s.Hkv, s.d, s.k_max, s.bs, self.num_splits)
+        # zero-filled once: the step's counters return to zero after every launch
+        self.step_ws = torch.zeros((max(sws, 16) + 3) // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((s.B, s.Hq, s.d), dtype=out_dtype, device=dev)
         self.lse = torch.empty((s.B, s.Hq), dtype=torch.float32, device=dev)
 
@@ -66,12 +69,24 @@ class DecodePlan:
                                 self.n_sel if n_sel is None else n_sel, self.shape.bs, self.softmax_scale,
                                 self.out, self.lse, self.decode_ws, self.num_splits, stream=stream)
 
-    def step(self, q, k, v, seqlens, kpool, wq, wk, stream=None):
-        """Gate, select and sparse-decode one step; returns (out, lse) views of the plan's buffers."""
-        self.gate(q, wq, wk, kpool, seqlens, stream)
-        self.select(seqlens, stream)
-        self.decode(q, k, v, seqlens, stream=stream)
+    def step(self, q, k, v, seqlens, kpool, wq, wk, stream=None, fused: bool = False):
+        """Gate, select and sparse-decode one step; returns (out, lse) views of the plan's buffers.
+
+        fused: one persistent launch (seer_decode_step); otherwise the three separate calls."""
+        if fused:
+            s = self.shape
+            seer.seer_decode_step(q, k, v, seqlens, kpool, wq, wk, s.bs, s.budget, self.gate_scale,
+                                  self.softmax_scale, self.scores, self.block_idx, self.n_sel, self.out, self.lse,
+                                  self.step_ws, self.num_splits, stream=stream)
+        else:
+            self.gate(q, wq, wk, kpool, seqlens, stream)
+            self.select(seqlens, stream)
+            self.decode(q, k, v, seqlens, stream=stream)
         return self.out, self.lse
+
+    def step_status(self, stream=None) -> int:
+        """0 while every fused step on this plan's workspace ran to completion."""
+        return seer.seer_decode_step_status(self.step_ws, stream=stream)
 
 
 def full_pool_lists(seqlens_host: torch.Tensor, bs: int, device="cuda"):

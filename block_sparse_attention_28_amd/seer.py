@@ -33,6 +33,10 @@ SIGNATURES = {
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
+    "seer_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "seer_decode_step": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _F, _P, _I, _I, _I, _I,
+                              _I, _I, _I, _F, _I, _P, _P, _P, _P, _SZ, _P, _I, _P, _P]),
+    "seer_decode_step_status": (_I, [_P, _P, _P]),
     "seer_block_sparse_prefill_kmax_row": (_I, [_I, _I, _I, _I]),
     "seer_block_sparse_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "seer_block_sparse_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _F, _I, _I, _P, _P, _I, _I, _F,
@@ -171,3 +175,33 @@ def seer_block_sparse_prefill(q, k, v, block_size: int, wq, wk, gate_scale: floa
           float(gate_scale), keep_num, keep_den, _ptr(kv_blocks), _ptr(kv_count), kv_blocks.shape[-1],
           1 if use_given_blocks else 0, float(softmax_scale), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
           _stream(stream))
+
+
+def seer_decode_step_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: int, block_size: int,
+                                    num_splits: int = 0) -> int:
+    return load().seer_decode_step_workspace_size(B, Hq, Hkv, d, k_max, block_size, num_splits)
+
+
+def seer_decode_step(q, k, v, seqlens, kpool, wq, wk, block_size: int, budget_tokens: int, gate_scale: float,
+                     softmax_scale: float, scores, block_idx, n_sel, out, lse=None, workspace=None,
+                     num_splits: int = 0, stream=None):
+    """Gate + select + sparse decode in one launch (same results as the three separate calls)."""
+    _bits(q), _bits(k), _bits(v), _bits(wq), _bits(wk)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    dg = wq.shape[1]
+    assert k.stride() == v.stride() and out.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
+    out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    k_max = budget_tokens // block_size
+    _call("seer_decode_step", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+          k.stride(2), cap, _ptr(seqlens), _ptr(wq), _ptr(wk), dg, float(gate_scale), _ptr(kpool), kpool.shape[2],
+          B, Hq, Hkv, d, block_size, int(budget_tokens), float(softmax_scale), int(num_splits), _ptr(scores),
+          _ptr(block_idx) if k_max else None, _ptr(n_sel), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
+          _ptr(lse), _stream(stream))
+
+
+def seer_decode_step_status(workspace, stream=None) -> int:
+    st = C.c_int(-1)
+    _call("seer_decode_step_status", _ptr(workspace), C.byref(st), _stream(stream))
+    return st.value

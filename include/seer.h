@@ -150,6 +150,40 @@ int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                        void *out, int out_dtype, float *lse, hipStream_t stream);
 
 /*
+ * One whole decode step in a single launch: the gate scores, the token-budget
+ * selection and the sparse decode with its merge -- the same results, bit for
+ * bit, as seer_gate_scores + seer_select_blocks + seer_sparse_decode with the
+ * same arguments, but run by one persistent grid whose workgroups pick up
+ * each (b, KV head)'s selection and decode as soon as that pair's inputs are
+ * ready (no kernel boundaries in between).
+ *   arguments as in the three calls above; scores [B][Hkv][nb_max],
+ *   block_idx [B][Hkv][budget_tokens / block_size] and n_sel [B][Hkv] are
+ *   written as those calls write them.
+ *   workspace >= seer_decode_step_workspace_size(...) bytes: control words and
+ *              per-pair counters, then the split partials.  It must be
+ *              zero-filled before its first use; every call leaves the
+ *              counters at zero again.  Calls sharing a workspace must be
+ *              ordered on one stream.
+ * Every wait inside the launch is bounded: if one ever ran out (it cannot in a
+ * correct launch), the launch still ends, its results are invalid, and
+ * seer_decode_step_status reports 1 until the workspace is zero-filled again.
+ * nb_max <= 16128.
+ */
+size_t seer_decode_step_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
+                                       int num_splits);
+int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                     const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                     int kv_capacity, const int32_t *seqlens,
+                     const seer_bf16 *wq, const seer_bf16 *wk, int dg, float gate_scale,
+                     const float *kpool, int nb_max, int B, int Hq, int Hkv, int d, int block_size,
+                     int budget_tokens, float softmax_scale, int num_splits,
+                     float *scores, int32_t *block_idx, int32_t *n_sel,
+                     void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                     hipStream_t stream);
+/* Copies the step workspace's status word (0 = valid) to *status and synchronises `stream`. */
+int seer_decode_step_status(const void *workspace, int *status, hipStream_t stream);
+
+/*
  * Block-sparse causal prefill (SeerAttention, abstract v1: the gate pools Q and
  * K per block, projects both through learnable linear layers and multiplies
  * them into block scores; a block-sparse FlashAttention kernel attends only

@@ -141,3 +141,35 @@ def test_select_exact_with_ties(nc, k):
             ref = oracle.select_blocks(scores[b, h].astype(np.float64), k)
             assert n_sel[b, h].item() == len(ref)
             np.testing.assert_array_equal(idx[b, h, :len(ref)].cpu().numpy(), ref)
+
+
+FUSED_CASES = [TINY_DECODE, DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE,
+               DecodeWorkload(name="fused_tail_g2_d64", B=3, Hq=8, Hkv=4, d=64, bs=64, budget=384, seed=31,
+                              L_range=(100, 3000)),
+               DecodeWorkload(name="fused_empty", B=2, Hq=4, Hkv=1, d=128, bs=64, budget=0, seed=32, L=256)]
+
+
+@pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
+def test_fused_step_equals_separate_calls(w):
+    """seer_decode_step gives bit-for-bit the results of gate + select + decode launched separately,
+    twice in a row on one workspace (its counters must be back at zero after each launch)."""
+    run = build_and_run(w, fused=True)
+    p = run.plan
+    assert p.step_status() == 0
+    fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    p.step(run.q, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"],
+           run.cache["wk"], fused=False)
+    torch.cuda.synchronize()
+    sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    names = ("scores", "block_idx", "n_sel", "out", "lse")
+    for n, a, b in zip(names, fused, sep):
+        assert torch.equal(a, b), f"{n} differs between the fused and the separate path"
+    q2 = inputs.decode_query(w, 1, "cuda")
+    p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
+           fused=True)
+    torch.cuda.synchronize()
+    o2 = p.out.clone()
+    p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
+           fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, p.out) and p.step_status() == 0
