@@ -72,18 +72,6 @@ struct DecodeCfg {
     static_assert(CPL >= 1 && TPL >= 1 && TPLV >= 1, "tile shape");
 };
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor word 3 for plain 32-bit dword access (gfx9 family).
-constexpr int kBufferFlags = 0x00020000;
-
-// 16-byte non-temporal load at descriptor base + voff + soff (bytes); reads past
-// the descriptor's range return zero.
-__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4_t t = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ uint4 ldg16_stream(const uint16_t *p) {
     const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));

@@ -1,0 +1,273 @@
+// gate_select_items.hpp -- gate scores and token-budget selection of one
+// (b, KV head) by one workgroup.
+//
+// Same operation as gate_chunk_item over all rows of a pair followed by
+// select_pair_item (see gate_items.hpp and topk_wave.hpp for the definitions
+// this follows), arranged so that the scores never leave the workgroup:
+//
+//  1. Loads are issued in the order q, Wq, Wk, pooled keys.  The gate vector
+//     u = gate_scale * Wk^T (Wq qbar) only needs the first three, so its
+//     dependent chain (two small products and three barriers) runs while the
+//     pooled-key rows are still arriving.
+//  2. score_j = u . kp_j for the complete blocks, written to the scores output
+//     and, as order-preserving keys, to LDS.
+//  3. A block-wide 8-bit radix select over the LDS keys finds the k-th largest
+//     key T and how many keys equal to T to take (the lower ids among equal
+//     keys); one sweep in id order then places each kept id with ballot counts
+//     per wave, so block_idx comes out ascending.
+#pragma once
+
+#include "gate_items.hpp"
+#include "topk_wave.hpp"
+
+namespace seer {
+
+template <int D, int NT, int G = 1>
+struct GsCfg {
+    static constexpr int NW = NT / 64;        // waves
+    static constexpr int LPR = D / 4;         // lanes per pooled-key row (4 floats each)
+    static constexpr int ROWS = NT / LPR;     // rows per workgroup-wide load
+    // row loads in flight per thread (fewer where 1024 threads' registers also hold 8 query rows)
+    static constexpr int ITER = NT >= 1024 && D == 128 && G >= 8 ? 12 : 16;
+    static constexpr int RPB = ROWS * ITER;   // rows per batch
+    static constexpr int CH = D / 8;          // 16-byte bf16 chunks per weight row
+    static constexpr int RG = NT / CH;        // weight-row groups
+    static constexpr int WB = RG >= 128 ? 1 : 128 / RG;    // weight rows per thread per batch
+    static constexpr int NBW = (256 + WB * RG - 1) / (WB * RG);  // batches covering dg <= 256
+};
+
+template <int D, int NT>
+struct GsSmem {
+    float a[256];                   // Wq qbar
+    float u_part[GsCfg<D, NT>::NW][D];
+    float u[D];
+    int hist[3][256];                 // radix histograms, used in rotation
+    int wcnt[2][2][GsCfg<D, NT>::NW];  // per-wave counts of the id sweep, double-buffered
+};
+
+struct GateSelectArgs {
+    GateArgs gate;
+    int k_max;
+    int32_t *block_idx;  // [pairs, k_max]
+    int32_t *n_sel;      // [pairs]
+};
+
+// Every thread of the NT-thread workgroup calls it; keys: LDS scratch of nb_max
+// words.  G query heads per KV head; dg <= 256.
+template <int D, int G, int NT, class Mem>
+__device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int pair, GsSmem<D, NT> &sm,
+                                                 uint32_t *keys) {
+    using C = GsCfg<D, NT, G>;
+    const GateArgs &ga = gs.gate;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Hkv = ga.Hkv, dg = ga.dg, nb_max = ga.nb_max;
+    const int b = pair / Hkv, g = pair % Hkv;
+    const int L = ga.seqlens[b];  // needed only once the scores exist
+
+    // 1. Loads: q chunk, first weight rows, first pooled-key rows.  Row indices
+    // past the data are clamped to its last row (their values are masked or
+    // discarded later), so no branch separates the loads, none waits for the
+    // context length, and all of them stay in flight together.
+    const int c = tid % C::CH, rg = tid / C::CH;
+    const auto qrs = buffer_rsrc(ga.q + b * ga.sq_b + (int64_t)(g * G) * ga.sq_h,
+                                 (uint32_t)(((int64_t)(G - 1) * ga.sq_h + D) * 2));
+    const auto wqrs = buffer_rsrc(ga.wq + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
+    const auto wkrs = buffer_rsrc(ga.wk + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
+    uint4 qw[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) qw[h] = buf_ld16(qrs, (uint32_t)(h * ga.sq_h * 2) + c * 16, 0);
+    auto wrow = [&](int r) { return (uint32_t)((r < dg ? r : dg - 1) * D * 2 + c * 16); };
+    uint4 wqv[C::WB], wkv[C::WB];
+#pragma unroll
+    for (int i = 0; i < C::WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(rg + i * C::RG), 0);
+#pragma unroll
+    for (int i = 0; i < C::WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the u inputs first
+    const int lr = tid / C::LPR, lc = tid % C::LPR;
+    const auto kprs = buffer_rsrc(ga.kpool + (int64_t)pair * nb_max * D, (uint32_t)nb_max * D * 4);
+    auto krow = [&](int j) { return (uint32_t)((j < nb_max ? j : nb_max - 1) * D * 4 + lc * 16); };
+    float4 x[C::ITER];
+#pragma unroll
+    for (int it = 0; it < C::ITER; ++it) x[it] = as_float4(buf_ld16_nt(kprs, krow(lr + it * C::ROWS), 0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. u = gate_scale * Wk^T (Wq qbar), qbar = mean of the group's query heads.
+    float qb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float f[8];
+        unpack8(qw[h], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[e] += f[e];
+    }
+    const float inv_g = 1.0f / (float)G;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[e] *= inv_g;
+#pragma unroll
+    for (int bw = 0; bw < C::NBW; ++bw) {  // a[r] = Wq[r] . qbar
+        const int r0 = bw * C::WB * C::RG;
+        if (bw > 0 && r0 >= dg) break;
+        if (bw > 0) {
+#pragma unroll
+            for (int i = 0; i < C::WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(r0 + rg + i * C::RG), 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::WB; ++i) {
+            const int r = r0 + rg + i * C::RG;
+            float f[8];
+            unpack8(wqv[i], f);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(f[e], qb[e], s);
+            s = group_sum<C::CH>(s);  // the CH lanes of a row group share r
+            if (c == 0 && r < dg) sm.a[r] = s;
+        }
+    }
+    if (tid < 256) sm.hist[0][tid] = 0;  // first radix histogram, ordered by the barriers below
+    __syncthreads();
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bw = 0; bw < C::NBW; ++bw) {  // u += a[r] * Wk[r]
+        const int r0 = bw * C::WB * C::RG;
+        if (bw > 0 && r0 >= dg) break;
+        if (bw > 0) {
+#pragma unroll
+            for (int i = 0; i < C::WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(r0 + rg + i * C::RG), 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::WB; ++i) {
+            const int r = r0 + rg + i * C::RG;
+            float f[8];
+            unpack8(wkv[i], f);
+            const float ar = r < dg ? sm.a[r] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(ar, f[e], acc[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float s = cross_group_sum<C::CH>(acc[e]);  // row groups of this wave
+        if (lane < C::CH) sm.u_part[wave][c * 8 + e] = s;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) s += sm.u_part[w][tid];
+        sm.u[tid] = s * ga.gate_scale;
+    }
+    __syncthreads();
+
+    // 3. score_j = u . kp_j for the complete blocks, batch by batch; -inf after them.
+    int nc = (L < 0 ? 0 : L) / ga.block_size;
+    nc = nc > nb_max ? nb_max : nc;
+    nc = __builtin_amdgcn_readfirstlane(nc);
+    float *srow = ga.scores + (int64_t)pair * nb_max;
+    for (int j = nc + tid; j < nb_max; j += NT) Mem::stf(srow + j, -INFINITY);
+    const float4 uu = reinterpret_cast<const float4 *>(sm.u)[lc];
+    for (int j0 = 0;;) {
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it) {
+            const int j = j0 + lr + it * C::ROWS;
+            float s = uu.x * x[it].x;
+            s = fmaf(uu.y, x[it].y, s);
+            s = fmaf(uu.z, x[it].z, s);
+            s = fmaf(uu.w, x[it].w, s);
+            s = group_sum<16>(s);
+            if constexpr (C::LPR == 32) s = sum_xor16(s);
+            if (lc == 0 && j < nc) {
+                Mem::stf(srow + j, s);
+                keys[j] = order_key(s);
+            }
+        }
+        j0 += C::RPB;
+        if (j0 >= nc) break;
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it) x[it] = as_float4(buf_ld16_nt(kprs, krow(j0 + lr + it * C::ROWS), 0));
+    }
+    __syncthreads();  // keys complete
+
+    // 4. Selection: k = min(k_max, nc) blocks, ids ascending, -1 after.
+    const int k_max = gs.k_max;
+    const int k = k_max < nc ? k_max : nc;
+    int32_t *out = gs.block_idx + (int64_t)pair * k_max;
+    if (k == nc || k == 0) {  // every complete block, or none, is kept
+        for (int i = tid; i < k_max; i += NT) Mem::sti(out + i, i < k ? i : -1);
+    } else {
+        // Radix passes over 8-bit digits from the top.  Every wave scans the
+        // histogram itself (one barrier per pass); histograms rotate over three
+        // buffers so the one zeroed during a pass was last read two passes ago.
+        uint32_t prefix = 0;
+        int need = k;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+            int *hist = sm.hist[pass % 3];
+            if (tid < 256) sm.hist[(pass + 1) % 3][tid] = 0;
+            for (int j = tid; j < nc; j += NT) {
+                const uint32_t key = keys[j];
+                if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+            }
+            __syncthreads();
+            // lane l covers digits 255-4l .. 252-4l, in descending order
+            int cnt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - 4 * lane - i];
+            const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+            const int incl = wave_inclusive_scan(local, lane);
+            const int excl = incl - local;
+            int digit = 0, rest = 0;
+            {
+                int cum = excl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (cum < need && cum + cnt[i] >= need) {  // the one digit where the count crosses need
+                        digit = 255 - 4 * lane - i;
+                        rest = need - cum;
+                    }
+                    cum += cnt[i];
+                }
+            }
+            const uint64_t hit = __ballot(excl < need && incl >= need);  // exactly one lane
+            const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+            prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, src) << shift;
+            need = __builtin_amdgcn_readlane(rest, src);
+        }
+        // Keep keys > T and the first `need` keys == T in id order; the position of a
+        // kept id is the number of kept ids below it.
+        const uint32_t T = prefix;
+        int gt_seen = 0, eq_seen = 0;
+        for (int base = 0, round = 0; base < nc; base += NT, round ^= 1) {
+            const int j = base + tid;
+            const uint32_t key = j < nc ? keys[j] : 0u;
+            const bool gt = j < nc && key > T, eq = j < nc && key == T;
+            const uint64_t gt_mask = __ballot(gt), eq_mask = __ballot(eq);
+            if (lane == 0) {
+                sm.wcnt[round][0][wave] = __popcll(gt_mask);
+                sm.wcnt[round][1][wave] = __popcll(eq_mask);
+            }
+            __syncthreads();
+            int gt_below = gt_seen + lanes_below(gt_mask), eq_below = eq_seen + lanes_below(eq_mask);
+            int gt_all = gt_seen, eq_all = eq_seen;
+#pragma unroll
+            for (int w = 0; w < C::NW; ++w) {
+                const int cg = sm.wcnt[round][0][w], ce = sm.wcnt[round][1][w];
+                if (w < wave) {
+                    gt_below += cg;
+                    eq_below += ce;
+                }
+                gt_all += cg;
+                eq_all += ce;
+            }
+            if (gt || (eq && eq_below < need)) Mem::sti(out + gt_below + (eq_below < need ? eq_below : need), j);
+            gt_seen = gt_all;
+            eq_seen = eq_all;
+        }
+        for (int i = k + tid; i < k_max; i += NT) Mem::sti(out + i, -1);
+    }
+    if (tid == 0) Mem::sti(gs.n_sel + pair, k);
+}
+
+}  // namespace seer

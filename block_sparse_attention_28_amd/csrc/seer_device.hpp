@@ -111,6 +111,30 @@ __device__ __forceinline__ float wave_max(float x) {
     return cross_group_max<16>(x);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor word 3 for plain 32-bit dword access (gfx9 family).
+constexpr int kBufferFlags = 0x00020000;
+
+// Descriptor over [base, base + bytes); loads past its range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
+}
+
+// 16-byte loads at descriptor base + voff + soff (bytes): cached, and
+// non-temporal (streamed past the caches' normal retention).
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t t = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t t = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float4 as_float4(uint4 u) {
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
 // Producer and consumer in different launches on one stream.
 struct LaunchMem {
     __device__ static int ldi(const int32_t *p) { return *p; }

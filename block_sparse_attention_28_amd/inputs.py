@@ -103,6 +103,23 @@ def decode_query(w: DecodeWorkload, step: int = 0, device="cpu") -> torch.Tensor
     return _normal_bf16((w.B, w.Hq, w.d), g, src_dev).to(device)
 
 
+def gate_inputs(B: int, Hq: int, Hkv: int, d: int, dg: int, nb_max: int, seed: int, device="cpu",
+                repeat_rows: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of the gate alone: q [B, Hq, d] bf16 ~ N(0, 1), gate weights [Hkv, dg, d] bf16
+    ~ N(0, 1/d), and a pooled-key table [B, Hkv, nb_max, d] fp32 ~ N(0, 1/64) (the spread of
+    a mean over 64 unit-variance keys).  repeat_rows > 0 copies rows j mod repeat_rows into
+    every row j, so that many blocks score exactly alike."""
+    g = _gen(seed * 1_000_033 + 5, device)
+    out = {"q": _normal_bf16((B, Hq, d), g, device)}
+    out["wq"] = _normal_bf16((Hkv, dg, d), g, device, std=1.0 / math.sqrt(d))
+    out["wk"] = _normal_bf16((Hkv, dg, d), g, device, std=1.0 / math.sqrt(d))
+    kp = torch.randn((B, Hkv, nb_max, d), generator=g, device=device, dtype=torch.float32).mul_(0.125)
+    if repeat_rows > 0:
+        kp = kp[:, :, torch.arange(nb_max, device=device) % repeat_rows].contiguous()
+    out["kpool"] = kp
+    return out
+
+
 def prefill_inputs(w: PrefillWorkload, device="cpu") -> Dict[str, torch.Tensor]:
     """Q, K, V [B, H, L, d] bf16 ~ N(0, 1) and gate weights [H, dg, d] bf16 ~ N(0, 1/d)."""
     shape = (w.B, w.H, w.L, w.d)

@@ -64,24 +64,35 @@ class DecodePlan:
         seer.seer_select_blocks(self.scores, seqlens, self.shape.bs, self.shape.budget, self.block_idx,
                                 self.n_sel, stream=stream)
 
+    def gate_select(self, q, wq, wk, kpool, seqlens, stream=None):
+        seer.seer_gate_select(q, wq, wk, kpool, seqlens, self.shape.bs, self.gate_scale, self.shape.budget,
+                              self.scores, self.block_idx, self.n_sel, stream=stream)
+
     def decode(self, q, k, v, seqlens, block_idx=None, n_sel=None, stream=None):
         seer.seer_sparse_decode(q, k, v, seqlens, self.block_idx if block_idx is None else block_idx,
                                 self.n_sel if n_sel is None else n_sel, self.shape.bs, self.softmax_scale,
                                 self.out, self.lse, self.decode_ws, self.num_splits, stream=stream)
 
-    def step(self, q, k, v, seqlens, kpool, wq, wk, stream=None, fused: bool = False):
+    def step(self, q, k, v, seqlens, kpool, wq, wk, stream=None, mode: str = "gate_select"):
         """Gate, select and sparse-decode one step; returns (out, lse) views of the plan's buffers.
 
-        fused: one persistent launch (seer_decode_step); otherwise the three separate calls."""
-        if fused:
+        mode "gate_select": seer_gate_select then seer_sparse_decode;
+        "calls": seer_gate_scores, seer_select_blocks, seer_sparse_decode;
+        "fused": one persistent launch (seer_decode_step), bit-for-bit the "calls" results."""
+        if mode == "fused":
             s = self.shape
             seer.seer_decode_step(q, k, v, seqlens, kpool, wq, wk, s.bs, s.budget, self.gate_scale,
                                   self.softmax_scale, self.scores, self.block_idx, self.n_sel, self.out, self.lse,
                                   self.step_ws, self.num_splits, stream=stream)
-        else:
+        elif mode == "calls":
             self.gate(q, wq, wk, kpool, seqlens, stream)
             self.select(seqlens, stream)
             self.decode(q, k, v, seqlens, stream=stream)
+        elif mode == "gate_select":
+            self.gate_select(q, wq, wk, kpool, seqlens, stream)
+            self.decode(q, k, v, seqlens, stream=stream)
+        else:
+            raise ValueError(f"unknown step mode {mode!r}")
         return self.out, self.lse
 
     def step_status(self, stream=None) -> int:

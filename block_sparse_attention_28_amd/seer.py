@@ -29,6 +29,7 @@ SIGNATURES = {
     "seer_pool_k_blocks": (_I, [_P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _P]),
     "seer_gate_scores": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
     "seer_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "seer_gate_select": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "seer_sparse_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
@@ -126,6 +127,19 @@ def seer_select_blocks(scores, seqlens, block_size: int, budget_tokens: int, blo
     _call("seer_select_blocks", _ptr(scores), _ptr(seqlens), B, H, nb_max, block_size, budget_tokens,
           _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel),
           _stream(stream))
+
+
+def seer_gate_select(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, budget_tokens: int, scores,
+                     block_idx, n_sel, stream=None):
+    """seer_gate_scores then seer_select_blocks on those scores, in one launch where the shape allows."""
+    _bits(q), _bits(wq), _bits(wk)
+    B, Hq, d = q.shape
+    Hkv, dg, _ = wq.shape
+    assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
+    assert n_sel.is_contiguous()
+    _call("seer_gate_select", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
+          kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), budget_tokens, _ptr(scores),
+          _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel), _stream(stream))
 
 
 def seer_sparse_decode_num_splits(B: int, Hkv: int, k_max: int, block_size: int, num_splits: int = 0) -> int:

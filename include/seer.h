@@ -119,6 +119,23 @@ int seer_select_blocks(const float *scores, const int32_t *seqlens, int B, int H
                        hipStream_t stream);
 
 /*
+ * Gate scores and token-budget selection together: the results of
+ * seer_gate_scores followed by seer_select_blocks on the scores it wrote
+ * (H = Hkv), arguments as there.  When B * Hkv is at least a quarter of the
+ * device's compute units, Hq / Hkv is 1, 2, 4 or 8 and nb_max <= 12288, one workgroup per
+ * (b, KV head) computes the scores and selects from them in LDS in a single
+ * launch; otherwise the two calls run.  The one-launch form reduces u in
+ * another order, so its scores may differ from seer_gate_scores' in the last
+ * bits; its selection is always exactly seer_select_blocks' on the scores it
+ * returns.
+ */
+int seer_gate_select(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                     const seer_bf16 *wq, const seer_bf16 *wk, int dg,
+                     const float *kpool, int nb_max, const int32_t *seqlens,
+                     int B, int Hq, int Hkv, int d, int block_size, float gate_scale, int budget_tokens,
+                     float *scores, int32_t *block_idx, int32_t *n_sel, hipStream_t stream);
+
+/*
  * Sparse decode over the kept blocks (SeerAttention-R abstract: the sparse
  * decoding kernel reads only the gate's blocks).  For query head h of
  * sequence b, with KV head g = h / G, the token set is

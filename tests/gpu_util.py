@@ -41,8 +41,8 @@ class GpuRun:
 
 
 def build_and_run(w: DecodeWorkload, step: int = 0, num_splits: int = 0, out_dtype=torch.bfloat16,
-                  device="cuda", seqlens=None, fused: bool = False) -> GpuRun:
-    say(f"[gpu] workload={w.name} step={step} splits={num_splits} out={out_dtype} fused={fused}")
+                  device="cuda", seqlens=None, mode: str = "gate_select") -> GpuRun:
+    say(f"[gpu] workload={w.name} step={step} splits={num_splits} out={out_dtype} mode={mode}")
     cache = inputs.decode_cache(w, device, seqlens=seqlens)
     q = inputs.decode_query(w, step, device)
     cap = cache["k"].shape[2]
@@ -52,7 +52,7 @@ def build_and_run(w: DecodeWorkload, step: int = 0, num_splits: int = 0, out_dty
     kpool = torch.zeros((w.B, w.Hkv, nb_max, w.d), dtype=torch.float32, device=device)
     ub, uj = pipeline.full_pool_lists(cache["seqlens"].cpu(), w.bs, device)
     plan.pool(cache["k"], kpool, ub, uj)
-    plan.step(q, cache["k"], cache["v"], cache["seqlens"], kpool, cache["wq"], cache["wk"], fused=fused)
+    plan.step(q, cache["k"], cache["v"], cache["seqlens"], kpool, cache["wq"], cache["wk"], mode=mode)
     torch.cuda.synchronize()
     return GpuRun(w, cache, q, kpool, plan, nb_max)
 

@@ -94,3 +94,12 @@ def test_other_calls_reject_bad_arguments(lib):
     # select: too many blocks for the LDS key buffer; missing outputs
     assert lib.seer_select_blocks(FAKE, FAKE, 2, 8, 20000, 64, 4096, FAKE, FAKE, NULL) == -2
     assert lib.seer_select_blocks(FAKE, FAKE, 2, 8, 512, 64, 4096, NULL, FAKE, NULL) == -1
+    # gate + select: dg too large, missing block ids with a nonzero budget, unsupported head_dim
+    gs = [FAKE, 4096, 128, FAKE, FAKE, 300, FAKE, 16, FAKE, 2, 32, 8, 128, 64, C.c_float(0.1), 1024, FAKE, FAKE,
+          FAKE, NULL]
+    assert lib.seer_gate_select(*gs) == -1
+    gs[5] = 128
+    gs[17] = NULL
+    assert lib.seer_gate_select(*gs) == -1
+    gs[17], gs[12], gs[1], gs[2] = FAKE, 96, 32 * 96, 96
+    assert lib.seer_gate_select(*gs) == -2

@@ -153,12 +153,12 @@ FUSED_CASES = [TINY_DECODE, DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE,
 def test_fused_step_equals_separate_calls(w):
     """seer_decode_step gives bit-for-bit the results of gate + select + decode launched separately,
     twice in a row on one workspace (its counters must be back at zero after each launch)."""
-    run = build_and_run(w, fused=True)
+    run = build_and_run(w, mode="fused")
     p = run.plan
     assert p.step_status() == 0
     fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(run.q, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"],
-           run.cache["wk"], fused=False)
+           run.cache["wk"], mode="calls")
     torch.cuda.synchronize()
     sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     names = ("scores", "block_idx", "n_sel", "out", "lse")
@@ -166,10 +166,10 @@ def test_fused_step_equals_separate_calls(w):
         assert torch.equal(a, b), f"{n} differs between the fused and the separate path"
     q2 = inputs.decode_query(w, 1, "cuda")
     p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
-           fused=True)
+           mode="fused")
     torch.cuda.synchronize()
     o2 = p.out.clone()
     p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
-           fused=False)
+           mode="calls")
     torch.cuda.synchronize()
     assert torch.equal(o2, p.out) and p.step_status() == 0

@@ -1,0 +1,92 @@
+"""GPU parity of seer_gate_select (gate scores and token-budget selection of each
+(b, KV head) in one launch) through the C ABI.
+
+Scores are compared with the fp64 oracle gate; the selection must be exactly the
+oracle's rule (k largest, ties to the lower id, ascending) applied to the
+scores the call returned, and exactly seer_select_blocks on those scores.
+Shapes have at least a quarter as many (b, KV head) pairs as the device has
+compute units, so the one-launch form runs, except the last (two calls)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_28_amd import inputs, seer
+
+from gpu_util import SCORE_REL, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    seer.load()
+
+
+# name, B, Hq, Hkv, d, bs, budget, nb_max, L (int or (lo, hi)), dg, repeat_rows, seed
+CASES = [
+    ("ragged_with_empty_and_dense", 16, 16, 4, 128, 64, 640, 48, (0, 3000), 128, 0, 61),
+    ("exact_ties_repeated_rows", 16, 16, 4, 128, 64, 640, 40, 2500, 128, 5, 62),
+    ("group8_d64_dg256", 8, 64, 8, 64, 128, 1280, 320, (1000, 40900), 256, 0, 63),
+    ("mha_group1", 1, 64, 64, 128, 64, 256, 80, 5000, 128, 0, 64),
+    ("budget_zero", 16, 16, 4, 64, 64, 0, 24, 1400, 64, 0, 65),
+    ("headline_shape", 16, 32, 8, 128, 128, 6553, 512, 65536, 128, 0, 66),
+    ("largest_one_launch_table", 16, 16, 4, 64, 64, 4096, 12288, (500000, 786432), 64, 0, 67),
+    ("two_calls_few_pairs", 2, 8, 2, 128, 64, 1024, 200, (3000, 12800), 128, 0, 68),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gate_select(case):
+    name, B, Hq, Hkv, d, bs, budget, nb_max, L, dg, rep, seed = case
+    say(f"[gpu] gate_select {name}")
+    x = inputs.gate_inputs(B, Hq, Hkv, d, dg, nb_max, seed, "cuda", repeat_rows=rep)
+    if isinstance(L, int):
+        seqlens = torch.full((B,), L, dtype=torch.int32)
+    else:
+        g = torch.Generator().manual_seed(seed)
+        seqlens = torch.randint(L[0], L[1] + 1, (B,), generator=g, dtype=torch.int32)
+    sl = seqlens.cuda()
+    k_max = budget // bs
+    scores = torch.full((B, Hkv, nb_max), float("nan"), device="cuda")
+    idx = torch.full((B, Hkv, max(k_max, 1)), -7, dtype=torch.int32, device="cuda")[..., :k_max]
+    n_sel = torch.full((B, Hkv), -7, dtype=torch.int32, device="cuda")
+    gscale = 1.0 / math.sqrt(dg)
+    seer.seer_gate_select(x["q"], x["wq"], x["wk"], x["kpool"], sl, bs, gscale, budget, scores,
+                          idx if k_max else None, n_sel)
+    # The selection of the same scores by the separate call.
+    idx2 = torch.full_like(idx, -9)
+    n2 = torch.full_like(n_sel, -9)
+    seer.seer_select_blocks(scores, sl, bs, budget, idx2 if k_max else None, n2)
+    torch.cuda.synchronize()
+    assert torch.equal(n_sel, n2) and torch.equal(idx, idx2), "selection differs from seer_select_blocks"
+
+    sc = scores.cpu().double().numpy()
+    gi, gn = idx.cpu().numpy(), n_sel.cpu().numpy()
+    q, wq, wk = host_bits(x["q"]), host_bits(x["wq"]), host_bits(x["wk"])
+    rng = np.random.default_rng(seed)
+    oracle_pairs = {(0, 0), (B - 1, Hkv - 1), (int(rng.integers(B)), int(rng.integers(Hkv)))}
+    G = Hq // Hkv
+    for b in range(B):
+        nc = min(int(seqlens[b]) // bs, nb_max)
+        k = min(k_max, nc)
+        for g in range(Hkv):
+            assert gn[b, g] == k
+            assert np.all(np.isneginf(sc[b, g, nc:])), "scores past the complete blocks must be -inf"
+            assert np.all(np.isfinite(sc[b, g, :nc]))
+            if k_max:
+                assert np.array_equal(gi[b, g, :k], oracle.select_blocks(sc[b, g, :nc], k)), (b, g)
+                assert np.all(gi[b, g, k:] == -1)
+            if (b, g) in oracle_pairs and nc:
+                kp = x["kpool"][b, g, :nc].cpu().double().numpy()
+                _, S = oracle.gate_scores(q[b, g * G:(g + 1) * G], wq[g], wk[g], kp, gscale)
+                rel = np.abs(sc[b, g, :nc] - S).max() / max(np.abs(S).max(), 1e-30)
+                assert rel <= SCORE_REL, f"scores b={b} g={g}: rel err {rel}"
+    if rep:
+        # Exact ties really occurred (and were resolved toward the lower ids above).
+        nc0 = min(int(seqlens[0]) // bs, nb_max)
+        assert len(np.unique(sc[0, 0, :nc0])) <= rep
