@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0 = skip)")
     ap.add_argument("--cpu-sequences", type=int, default=2)
     ap.add_argument("--prefill-steps", type=int, default=5, help="block-sparse prefill timing (0 = skip)")
+    ap.add_argument("--mode", default="gate_select", choices=("gate_select", "calls", "fused"),
+                    help="form of the timed step (the others are timed briefly for context)")
+    ap.add_argument("--mode-steps", type=int, default=16, help="steps per form in the context timing (0 = skip)")
+    ap.add_argument("--graph-steps", type=int, default=16, help="HIP-graph replays timed (0 = skip)")
+    ap.add_argument("--dense", type=int, default=1, help="also time the decode with every block kept (context)")
     return ap.parse_args()
 
 
@@ -87,6 +92,81 @@ def decode_bytes(w, seqlens_host):
     return kv, kv + q_out + ids
 
 
+def gate_bytes(w, seqlens_host):
+    """Algorithmic bytes of the gate and selection: fp32 pooled keys of the complete blocks,
+    the query, both gate weight matrices, and the scores written and read back."""
+    kp = sum(w.Hkv * (L // w.bs) * w.d * 4 for L in seqlens_host)
+    q = w.B * w.Hq * w.d * 2
+    wts = 2 * w.Hkv * w.gate_dim * w.d * 2
+    sc = 2 * sum(w.Hkv * (L // w.bs) * 4 for L in seqlens_host)
+    return kp + q + wts + sc
+
+
+def graph_step_us(plan, layers, steps, w, args):
+    """The gate_select + decode step captured once per layer as a HIP graph, then replayed.
+    Each replay's output is checked against the eager step's."""
+    R = len(layers)
+    g_q = torch.empty_like(steps[0]["q"])
+    g_sl = torch.empty_like(steps[0]["seqlens"])
+    graphs = []
+    for l in range(R):
+        c = layers[l].cache
+        g_q.copy_(steps[l]["q"])
+        g_sl.copy_(steps[l]["seqlens"])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.gate_select(g_q, c["wq"], c["wk"], layers[l].kpool, g_sl)
+            plan.decode(g_q, c["k"], c["v"], g_sl)
+        graphs.append(g)
+    # replay vs eager on the first steps
+    for s in range(min(R, 4)):
+        lay = layers[steps[s]["layer"]]
+        c = lay.cache
+        plan.gate_select(steps[s]["q"], c["wq"], c["wk"], lay.kpool, steps[s]["seqlens"])
+        plan.decode(steps[s]["q"], c["k"], c["v"], steps[s]["seqlens"])
+        torch.cuda.synchronize()
+        ref = plan.out.clone()
+        g_q.copy_(steps[s]["q"])
+        g_sl.copy_(steps[s]["seqlens"])
+        graphs[steps[s]["layer"]].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ref, plan.out), "graph replay differs from the eager step"
+    n = args.graph_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(n):
+        graphs[s % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / n, 2)
+
+
+def dense_decode_us(w, lay, base_L, dev):
+    """Context line: the same decode with every complete block kept (budget = context)."""
+    nb_max = lay.nb_max
+    L = int(base_L.max())
+    shape = pipeline.DecodeShape(w.B, w.Hq, w.Hkv, w.d, w.bs, L, nb_max, w.gate_dim)
+    dp = pipeline.DecodePlan(shape, dev)
+    sl = base_L.to(torch.int32).to(dev)
+    q = inputs.decode_query(w, 0, dev)
+    dp.gate_select(q, lay.cache["wq"], lay.cache["wk"], lay.kpool, sl)
+    for _ in range(2):
+        dp.decode(q, lay.cache["k"], lay.cache["v"], sl)
+    torch.cuda.synchronize()
+    n = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        dp.decode(q, lay.cache["k"], lay.cache["v"], sl)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    kv = sum(w.Hkv * int(x) * w.d * 2 * 2 for x in base_L.tolist())
+    return {"us": round(us, 1), "kept_blocks": int(base_L.min()) // w.bs,
+            "effective_GBps": round(kv / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -124,22 +204,33 @@ def main():
                    torch.tensor([d[1] for d in done], dtype=torch.int32, device=dev))
         steps.append({"layer": l, "seqlens": L.to(torch.int32).to(dev), "L": L.tolist(), "upd": upd,
                       "q": inputs.decode_query(w, s, dev)})
+    # Each step's launches with their arguments converted once (host marshalling stays out of the loop).
+    for st in steps:
+        lay = layers[st["layer"]]
+        c = lay.cache
+        st["pool"] = seer.seer_pool_k_blocks(c["k"], *st["upd"], lay.kpool, w.bs, bind=True) if st["upd"] else None
+        st["calls"] = {m: plan.bind_step(st["q"], c["k"], c["v"], st["seqlens"], lay.kpool, c["wq"], c["wk"], mode=m)
+                       for m in ("calls", "gate_select", "fused")}
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
+    mode = args.mode
 
-    def run_step(s):
+    def run_step(s, mode=mode, events=False):
         st = steps[s]
-        lay = layers[st["layer"]]
-        c = lay.cache
-        if st["upd"] is not None:
-            plan.pool(c["k"], lay.kpool, *st["upd"])
-        plan.gate(st["q"], c["wq"], c["wk"], lay.kpool, st["seqlens"])
-        plan.select(st["seqlens"])
-        ev[s][0].record(stream)
-        plan.decode(st["q"], c["k"], c["v"], st["seqlens"])
-        ev[s][1].record(stream)
+        if events:
+            ev[s][0].record(stream)
+        if st["pool"] is not None:
+            st["pool"]()
+        calls = st["calls"][mode]
+        for call in calls[:-1]:
+            call()
+        if events:
+            ev[s][1].record(stream)
+        calls[-1]()  # the decode (or the whole fused step)
+        if events:
+            ev[s][2].record(stream)
 
     # A plain elementwise copy of known size (read 256 MiB, write 256 MiB): the
     # reference point that scales hardware byte counters under a profiler.
@@ -156,17 +247,47 @@ def main():
         run_step(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # The same steps again with events around each step and its last launch.
+    for s in range(W, total):
+        run_step(s, events=True)
+    torch.cuda.synchronize()
 
     ms_per_step = elapsed * 1e3 / K
     kv_bytes = [decode_bytes(w, steps[s]["L"]) for s in range(W, total)]
-    dec_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(W, total)]
+    step_us = sorted(ev[s][0].elapsed_time(ev[s][2]) * 1e3 for s in range(W, total))
     mean_kv = sum(b[0] for b in kv_bytes) / K
     mean_alg = sum(b[1] for b in kv_bytes) / K
-    dec_avg_ms = sum(dec_ms) / K
     value = mean_kv / (ms_per_step * 1e-3) / 1e9
-    achieved = mean_alg / (dec_avg_ms * 1e-3) / 1e9
+    dom_us = sum(ev[s][1].elapsed_time(ev[s][2]) * 1e3 for s in range(W, total)) / K
+    if mode == "fused":
+        # one launch does the whole step: its algorithmic bytes include the gate's reads
+        dom_bytes = mean_alg + gate_bytes(w, steps[W]["L"])
+        dom_name = "decode_step_kernel (seer_decode_step: gate, select, split decode, merge)"
+    else:
+        dom_bytes = mean_alg
+        dom_name = "seer_sparse_decode (split kernel + LSE merge kernel)"
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     kept = min(w.k_max, int(base_L.min()) // w.bs)
     ncb = int(base_L.min()) // w.bs
+
+    # Context: the other step forms on the same layers, and the step replayed as a HIP graph.
+    modes_us = {}
+    for m in ("calls", "gate_select", "fused"):
+        if args.mode_steps <= 0:
+            break
+        n = min(args.mode_steps, total)
+        for s in range(min(2, n)):
+            run_step(s, m)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(n):
+            run_step(s, m)
+        e1.record()
+        torch.cuda.synchronize()
+        modes_us[m] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+    graph_us = graph_step_us(plan, layers, steps, w, args) if args.graph_steps > 0 else None
+    dense = dense_decode_us(w, layers[0], base_L, dev) if args.dense else None
 
     line = {
         "metric": METRIC,
@@ -187,12 +308,16 @@ def main():
                    "context": int(base_L[0]) if w.L else [int(base_L.min()), int(base_L.max())],
                    "block_size": w.bs, "budget_tokens": w.budget, "kept_blocks": kept,
                    "sparsity": round(1.0 - kept / max(ncb, 1), 4), "layers_rotated": R,
-                   "num_splits": plan.num_splits},
-        "decode_us": round(dec_avg_ms * 1e3, 2),
-        "roofline": {"kernel": "seer_sparse_decode (split kernel + LSE merge kernel)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "bytes_per_launch": int(mean_alg)},
+                   "num_splits": plan.num_splits, "step_form": mode},
+        "step_gpu_us": {"p10": round(step_us[K // 10], 2), "p50": round(step_us[K // 2], 2),
+                        "p90": round(step_us[(9 * K) // 10], 2)},
+        "step_forms_us": modes_us,
+        "graph_step_us": graph_us,
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name) if mode != "fused" else None,
+                     "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
+        "dense_decode": dense,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)

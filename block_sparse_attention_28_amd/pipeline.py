@@ -95,6 +95,29 @@ class DecodePlan:
             raise ValueError(f"unknown step mode {mode!r}")
         return self.out, self.lse
 
+    def bind_step(self, q, k, v, seqlens, kpool, wq, wk, mode: str = "gate_select", stream=None):
+        """The launches of one step (as in step()) with their arguments converted once:
+        a list of callables, each launching one library call again."""
+        s = self.shape
+        if mode == "fused":
+            return [seer.seer_decode_step(q, k, v, seqlens, kpool, wq, wk, s.bs, s.budget, self.gate_scale,
+                                          self.softmax_scale, self.scores, self.block_idx, self.n_sel, self.out,
+                                          self.lse, self.step_ws, self.num_splits, stream=stream, bind=True)]
+        if mode == "calls":
+            calls = [seer.seer_gate_scores(q, wq, wk, kpool, seqlens, s.bs, self.gate_scale, self.scores,
+                                           stream=stream, bind=True),
+                     seer.seer_select_blocks(self.scores, seqlens, s.bs, s.budget, self.block_idx, self.n_sel,
+                                             stream=stream, bind=True)]
+        elif mode == "gate_select":
+            calls = [seer.seer_gate_select(q, wq, wk, kpool, seqlens, s.bs, self.gate_scale, s.budget, self.scores,
+                                           self.block_idx, self.n_sel, stream=stream, bind=True)]
+        else:
+            raise ValueError(f"unknown step mode {mode!r}")
+        calls.append(seer.seer_sparse_decode(q, k, v, seqlens, self.block_idx, self.n_sel, s.bs, self.softmax_scale,
+                                             self.out, self.lse, self.decode_ws, self.num_splits, stream=stream,
+                                             bind=True))
+        return calls
+
     def step_status(self, stream=None) -> int:
         """0 while every fused step on this plan's workspace ran to completion."""
         return seer.seer_decode_step_status(self.step_ws, stream=stream)

@@ -87,7 +87,27 @@ def _stream(stream) -> C.c_void_p:
     return C.c_void_p(s.cuda_stream)
 
 
-def _call(name: str, *args):
+class Bound:
+    """One library call with its arguments converted to C values once; calling the
+    object launches it again (for tight step loops where the marshalling would
+    otherwise cost more host time than the launch)."""
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name: str, args):
+        self.name = name
+        self.fn = getattr(load(), name)
+        types = SIGNATURES[name][1]
+        self.args = tuple(a if a is None or isinstance(a, C._SimpleCData) else t(a) for t, a in zip(types, args))
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SEER_OK:
+            raise SeerError(self.name, st)
+
+
+def _call(name: str, *args, bind: bool = False):
+    if bind:
+        return Bound(name, args)
     st = getattr(load(), name)(*args)
     if st != SEER_OK:
         raise SeerError(name, st)
@@ -99,47 +119,53 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
-def seer_pool_k_blocks(k, upd_b, upd_blk, kpool, block_size: int, stream=None):
+def seer_pool_k_blocks(k, upd_b, upd_blk, kpool, block_size: int, stream=None, bind: bool = False):
     """kpool[b, :, j] = mean of block j of k[b] for each listed (b, j).  k [B, Hkv, cap, d] bf16."""
     _bits(k)
     B, Hkv, cap, d = k.shape
     assert kpool.dtype == torch.float32 and kpool.is_contiguous() and kpool.shape[:2] == (B, Hkv)
     assert upd_b.dtype == torch.int32 and upd_blk.dtype == torch.int32 and upd_b.numel() == upd_blk.numel()
-    _call("seer_pool_k_blocks", _ptr(k), k.stride(0), k.stride(1), k.stride(2), B, Hkv, d, block_size, cap,
-          _ptr(upd_b), _ptr(upd_blk), upd_b.numel(), _ptr(kpool), kpool.shape[2], _stream(stream))
+    return _call(
+        "seer_pool_k_blocks", _ptr(k), k.stride(0), k.stride(1), k.stride(2), B, Hkv, d, block_size, cap,
+        _ptr(upd_b), _ptr(upd_blk), upd_b.numel(), _ptr(kpool), kpool.shape[2], _stream(stream), bind=bind)
 
 
-def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, scores, stream=None):
+def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, scores, stream=None,
+                     bind: bool = False):
     """scores [B, Hkv, nb_max] fp32 from q [B, Hq, d], wq/wk [Hkv, dg, d], kpool [B, Hkv, nb_max, d]."""
     _bits(q), _bits(wq), _bits(wk)
     B, Hq, d = q.shape
     Hkv, dg, _ = wq.shape
     assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
-    _call("seer_gate_scores", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
-          kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), _ptr(scores),
-          _stream(stream))
+    return _call(
+        "seer_gate_scores", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool), kpool.shape[2],
+        _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), _ptr(scores), _stream(stream), bind=bind)
 
 
-def seer_select_blocks(scores, seqlens, block_size: int, budget_tokens: int, block_idx, n_sel, stream=None):
+def seer_select_blocks(scores, seqlens, block_size: int, budget_tokens: int, block_idx, n_sel, stream=None,
+                       bind: bool = False):
     """block_idx [B, H, budget // bs] int32 (ascending, -1 padded), n_sel [B, H] int32."""
     B, H, nb_max = scores.shape
     assert scores.is_contiguous() and n_sel.is_contiguous()
-    _call("seer_select_blocks", _ptr(scores), _ptr(seqlens), B, H, nb_max, block_size, budget_tokens,
-          _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel),
-          _stream(stream))
+    return _call(
+        "seer_select_blocks", _ptr(scores), _ptr(seqlens), B, H, nb_max, block_size, budget_tokens,
+        _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel), _stream(stream),
+        bind=bind)
 
 
 def seer_gate_select(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, budget_tokens: int, scores,
-                     block_idx, n_sel, stream=None):
+                     block_idx, n_sel, stream=None, bind: bool = False):
     """seer_gate_scores then seer_select_blocks on those scores, in one launch where the shape allows."""
     _bits(q), _bits(wq), _bits(wk)
     B, Hq, d = q.shape
     Hkv, dg, _ = wq.shape
     assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
     assert n_sel.is_contiguous()
-    _call("seer_gate_select", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
-          kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), budget_tokens, _ptr(scores),
-          _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel), _stream(stream))
+    return _call(
+        "seer_gate_select", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool), kpool.shape[2],
+        _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), budget_tokens, _ptr(scores),
+        _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel), _stream(stream),
+        bind=bind)
 
 
 def seer_sparse_decode_num_splits(B: int, Hkv: int, k_max: int, block_size: int, num_splits: int = 0) -> int:
@@ -152,7 +178,7 @@ def seer_sparse_decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: 
 
 
 def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, softmax_scale: float, out,
-                       lse=None, workspace=None, num_splits: int = 0, stream=None):
+                       lse=None, workspace=None, num_splits: int = 0, stream=None, bind: bool = False):
     """out [B, Hq, d] (bf16 or fp32) = attention of q over the kept blocks + tail of k/v [B, Hkv, cap, d]."""
     _bits(q), _bits(k), _bits(v)
     B, Hq, d = q.shape
@@ -161,10 +187,11 @@ def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, soft
     k_max = block_idx.shape[2] if block_idx is not None else 0
     out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("seer_sparse_decode", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
-          k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
-          block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
-          _ptr(lse), _stream(stream))
+    return _call(
+        "seer_sparse_decode", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
+        block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
+        _ptr(lse), _stream(stream), bind=bind)
 
 
 def seer_block_sparse_prefill_kmax_row(L: int, block_size: int, keep_num: int, keep_den: int) -> int:
@@ -198,7 +225,7 @@ def seer_decode_step_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: in
 
 def seer_decode_step(q, k, v, seqlens, kpool, wq, wk, block_size: int, budget_tokens: int, gate_scale: float,
                      softmax_scale: float, scores, block_idx, n_sel, out, lse=None, workspace=None,
-                     num_splits: int = 0, stream=None):
+                     num_splits: int = 0, stream=None, bind: bool = False):
     """Gate + select + sparse decode in one launch (same results as the three separate calls)."""
     _bits(q), _bits(k), _bits(v), _bits(wq), _bits(wk)
     B, Hq, d = q.shape
@@ -208,11 +235,12 @@ def seer_decode_step(q, k, v, seqlens, kpool, wq, wk, block_size: int, budget_to
     out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
     ws_bytes = workspace.numel() * workspace.element_size()
     k_max = budget_tokens // block_size
-    _call("seer_decode_step", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
-          k.stride(2), cap, _ptr(seqlens), _ptr(wq), _ptr(wk), dg, float(gate_scale), _ptr(kpool), kpool.shape[2],
-          B, Hq, Hkv, d, block_size, int(budget_tokens), float(softmax_scale), int(num_splits), _ptr(scores),
-          _ptr(block_idx) if k_max else None, _ptr(n_sel), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
-          _ptr(lse), _stream(stream))
+    return _call(
+        "seer_decode_step", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        k.stride(2), cap, _ptr(seqlens), _ptr(wq), _ptr(wk), dg, float(gate_scale), _ptr(kpool), kpool.shape[2], B,
+        Hq, Hkv, d, block_size, int(budget_tokens), float(softmax_scale), int(num_splits), _ptr(scores),
+        _ptr(block_idx) if k_max else None, _ptr(n_sel), _ptr(workspace), ws_bytes, _ptr(out), out_dtype, _ptr(lse),
+        _stream(stream), bind=bind)
 
 
 def seer_decode_step_status(workspace, stream=None) -> int:

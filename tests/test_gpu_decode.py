@@ -173,3 +173,29 @@ def test_fused_step_equals_separate_calls(w):
            mode="calls")
     torch.cuda.synchronize()
     assert torch.equal(o2, p.out) and p.step_status() == 0
+
+
+def test_step_replays_as_hip_graph():
+    """gate_select + decode captured as a HIP graph: every replay (with eager work and
+    synchronisations in between) gives the eager step's results bit for bit."""
+    w = DECODE_L32K
+    run = build_and_run(w)
+    p, c = run.plan, run.cache
+    q = torch.empty_like(run.q)
+    q.copy_(run.q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        p.gate_select(q, c["wq"], c["wk"], run.kpool, c["seqlens"])
+        p.decode(q, c["k"], c["v"], c["seqlens"])
+    for step in range(3):
+        qs = inputs.decode_query(w, 10 + step, "cuda")
+        p.step(qs, c["k"], c["v"], c["seqlens"], run.kpool, c["wq"], c["wk"])
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (p.block_idx, p.n_sel, p.out, p.lse)]
+        p.out.zero_()
+        q.copy_(qs)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (p.block_idx, p.n_sel, p.out, p.lse)):
+            assert torch.equal(a, b), f"replay {step} differs from the eager step"
