@@ -52,6 +52,7 @@ def _bind(path: str):
         "so_gate_scores": (I, [P, I64, I, I, P, P, I, P, I, D, P, P]),
         "so_select_blocks": (I, [P, I, I, P]),
         "so_sparse_attention": (I, [P, I64, I, I, P, P, I64, I, I, P, I, D, P, P, P]),
+        "so_decode_block_mass": (I, [P, I64, I, I, P, P, I64, I, I, D, P, P, P]),
         "so_pool_cache": (I, [P, I64, I64, I64, P, I, I, I, I, I, P]),
         "so_decode_step": (I, [P, I64, I64, P, P, I64, I64, I64, P, I, I, I, I, I, I,
                                P, P, I, D, P, I, D, P, P, P, P, P]),
@@ -148,6 +149,24 @@ def sparse_attention(q, k, v, bs: int, idx, scale: float, L: Optional[int] = Non
     _check(_load().so_sparse_attention(_p(q), d, G, d, _p(k), _p(v), d, L, bs, _p(idx), idx.shape[0],
                                        float(scale), _p(out), _p(lse), _p(w)), "sparse_attention")
     return out, lse, w
+
+
+def decode_block_mass(q, k, v, bs: int, scale: float, L: Optional[int] = None):
+    """Ground truth of one KV head's decode: dense attention of q [G, d] over k/v [>=L, d].
+
+    Returns (out [G, d], lse [G], mass [L // bs + 1]): the group-mean attention mass of
+    every complete block, then of the tail (0 when L is a multiple of bs)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    G, d = q.shape
+    if L is None:
+        L = k.shape[0]
+    assert k.shape[0] >= L and v.shape == k.shape
+    out = np.zeros((G, d), dtype=np.float64)
+    lse = np.zeros((G,), dtype=np.float64)
+    mass = np.zeros((L // bs + 1,), dtype=np.float64)
+    _check(_load().so_decode_block_mass(_p(q), d, G, d, _p(k), _p(v), d, L, bs, float(scale), _p(out), _p(lse),
+                                        _p(mass)), "decode_block_mass")
+    return out, lse, mass
 
 
 def pool_cache(k, seqlens, bs: int, nb_max: int) -> np.ndarray:

@@ -241,6 +241,40 @@ int so_sparse_attention(const uint16_t *q, int64_t q_row_stride, int G, int d,
     return 0;
 }
 
+/* ---------------------------------------------------------- ground truth --- */
+int so_decode_block_mass(const uint16_t *q, int64_t q_row_stride, int G, int d,
+                         const uint16_t *k, const uint16_t *v, int64_t kv_row_stride,
+                         int L, int bs, double scale, double *out, double *lse, double *mass)
+{
+    if (!mass || G <= 0 || bs <= 0 || L < 0)
+        return -1;
+    const int nc = L / bs;
+    int32_t *all = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nc > 0 ? nc : 1));
+    double *w = (double *)malloc(sizeof(double) * (size_t)G * (size_t)(L > 0 ? L : 1));
+    if (!all || !w) {
+        free(all);
+        free(w);
+        return -2;
+    }
+    for (int j = 0; j < nc; ++j)
+        all[j] = j;
+    /* every complete block kept: T is the whole context */
+    int rc = so_sparse_attention(q, q_row_stride, G, d, k, v, kv_row_stride, L, bs, all, nc, scale, out, lse, w);
+    if (rc == 0) {
+        for (int j = 0; j <= nc; ++j) {
+            const int t0 = j * bs, t1 = j < nc ? (j + 1) * bs : L;
+            double sum = 0.0;
+            for (int h = 0; h < G; ++h)
+                for (int t = t0; t < t1; ++t)
+                    sum += w[(int64_t)h * L + t];
+            mass[j] = sum / G;
+        }
+    }
+    free(all);
+    free(w);
+    return rc;
+}
+
 /* ------------------------------------------------------ batched decode --- */
 int so_pool_cache(const uint16_t *k, int64_t sk_b, int64_t sk_h, int64_t sk_t,
                   const int32_t *seqlens, int B, int Hkv, int d, int bs, int nb_max,

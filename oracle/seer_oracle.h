@@ -19,6 +19,8 @@
  *         ties toward the lower block index, emitted in ascending order
  *     D5  token set T = kept blocks plus the incomplete tail [nc*bs, L)
  *     D6  softmax attention of every query head over T
+ *     G1  ground truth: attention mass of every block under dense attention,
+ *         averaged over the group's query heads
  *   prefill, per head
  *     P1  mean-pool Q and K over each bs-token block
  *     P2  S_ij = (Wq Qbar_i) . (Wk Kbar_j) * gate_scale for j <= i
@@ -70,6 +72,17 @@ int so_sparse_attention(const uint16_t *q, int64_t q_row_stride, int G, int d,
                         int L, int bs, const int32_t *idx, int n_idx, double scale,
                         double *out /* [G][d] */, double *lse /* [G] */,
                         double *w /* nullable, [G][L] */);
+
+/* G1, the block-level ground truth of decoding attention (SeerAttention v2
+ * abstract: the block-level ground truth of the attention map, extracted next
+ * to the attention itself).  Dense softmax attention of the group's G query
+ * rows over the whole context [0, L) (every complete block plus the tail);
+ * mass[j] = (1/G) sum_h sum_{t in block j} w_ht for j < nc = L / bs, and
+ * mass[nc] = the same sum over the tail [nc*bs, L) (0 when there is none).
+ * out [G][d] and lse [G] are that dense attention's.  mass has nc + 1 slots. */
+int so_decode_block_mass(const uint16_t *q, int64_t q_row_stride, int G, int d,
+                         const uint16_t *k, const uint16_t *v, int64_t kv_row_stride,
+                         int L, int bs, double scale, double *out, double *lse, double *mass);
 
 /* D1 over a batch: kpool [B][Hkv][nb_max][d], complete blocks filled, the rest zero. */
 int so_pool_cache(const uint16_t *k, int64_t sk_b, int64_t sk_h, int64_t sk_t,

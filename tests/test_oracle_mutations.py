@@ -15,6 +15,7 @@ import oracle
 
 import test_oracle_attention as T_att
 import test_oracle_gate_select as T_gs
+import test_oracle_ground_truth as T_gt
 import test_oracle_pipeline as T_pipe
 
 
@@ -63,6 +64,11 @@ MUTATIONS = [
      T_gs.test_pool_ramp_closed_form),
     ("keep count floors", "* keep_num + keep_den - 1) / keep_den;", "* keep_num) / keep_den + 1;",
      T_pipe.test_prefill_keep_counts_golden),
+    ("block mass summed instead of averaged over heads", "mass[j] = sum / G;", "mass[j] = sum;",
+     lambda: T_gt.test_block_mass_normalised_and_nonnegative(300, 64)),
+    ("tail share dropped from the ground truth", "const int t0 = j * bs, t1 = j < nc ? (j + 1) * bs : L;",
+     "const int t0 = j * bs, t1 = j < nc ? (j + 1) * bs : j * bs;",
+     lambda: T_gt.test_equal_keys_give_token_count_shares(300, 64)),
     ("prefill causal mask dropped", "for (int tt = 0; tt <= t; ++tt)", "for (int tt = 0; tt < L; ++tt)",
      lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
 ]
