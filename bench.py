@@ -167,6 +167,43 @@ def dense_decode_us(w, lay, base_L, dev):
             "effective_GBps": round(kv / (us * 1e-6) / 1e9, 1)}
 
 
+def ground_truth_context(w, lay, step, plan, dev):
+    """Block-level ground truth of the first step's attention (seer_decode_block_mass), its time,
+    and how much of the true attention mass the gate's selection captures."""
+    c = lay.cache
+    nb_max = lay.nb_max
+    mass = torch.empty((w.B, w.Hkv, nb_max + 1), dtype=torch.float32, device=dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    wsb = seer.seer_decode_block_mass_workspace_size(w.B, w.Hq, w.Hkv, w.d, nb_max, w.bs, 0)
+    ws = torch.zeros((wsb + 3) // 4, dtype=torch.float32, device=dev)
+    call = seer.seer_decode_block_mass(step["q"], c["k"], c["v"], step["seqlens"], w.bs, plan.softmax_scale, mass,
+                                       out, None, ws, bind=True)
+    call()
+    torch.cuda.synchronize()
+    n = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    plan.gate_select(step["q"], c["wq"], c["wk"], lay.kpool, step["seqlens"])
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    tail = mass[:, :, nb_max]
+    blocks = mass[:, :, :nb_max]
+    idx = plan.block_idx.long().clamp(min=0)
+    valid = (plan.block_idx >= 0).to(mass.dtype)
+    captured = (torch.gather(blocks, 2, idx) * valid).sum(-1) + tail
+    k = plan.n_sel.max().item()
+    best = blocks.topk(k, dim=-1).values.sum(-1) + tail
+    kbytes = sum(w.Hkv * int(x) * w.d * 2 * 2 for x in step["L"])
+    return {"call": "seer_decode_block_mass", "us": round(us, 1),
+            "effective_GBps": round(kbytes / (us * 1e-6) / 1e9, 1),
+            "gate_mass_recall": round(captured.mean().item(), 4),
+            "best_k_mass": round(best.mean().item(), 4),
+            "note": "attention mass of the kept blocks + tail under dense attention; gate weights are random"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -288,6 +325,7 @@ def main():
         modes_us[m] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
     graph_us = graph_step_us(plan, layers, steps, w, args) if args.graph_steps > 0 else None
     dense = dense_decode_us(w, layers[0], base_L, dev) if args.dense else None
+    gt = ground_truth_context(w, layers[0], steps[0], plan, dev) if args.dense else None
 
     line = {
         "metric": METRIC,
@@ -318,6 +356,7 @@ def main():
                      "traffic": measured_traffic(w.name) if mode != "fused" else None,
                      "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
         "dense_decode": dense,
+        "ground_truth": gt,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)

@@ -57,6 +57,79 @@ static int launch_decode(const DecodeArgs &a, int B, hipStream_t stream) {
     return launch_status();
 }
 
+// ---------------------------------------------------------- ground truth ----
+// Dense form of the split kernel (every complete block, then the tail) that
+// also records each unit's per-wave log-sum-exp; then the block masses.
+template <int D, int BS, int G>
+__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void block_mass_split_kernel(const DecodeArgs a) {
+    __shared__ DecodeSmem<D, BS, G> sm;
+    decode_split_item<D, BS, G, LaunchMem, true>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
+// One (b, KV head) per workgroup: mass of unit u = mean over the group's heads
+// of 2^(log2-sum-exp of the unit - log2-sum-exp of the whole context).
+template <int G>
+__global__ __launch_bounds__(256) void block_mass_kernel(const float *blk_lse, const float *lse, const int32_t *seqlens,
+                                                         int Hq, int Hkv, int kv_capacity, int block_size, int nb_max,
+                                                         float *mass) {
+    const int pair = blockIdx.x, b = pair / Hkv, g = pair % Hkv;
+    int L = seqlens[b];
+    L = L < 0 ? 0 : (L > kv_capacity ? kv_capacity : L);
+    int nc = L / block_size;
+    const bool tail = L - nc * block_size > 0;
+    nc = nc < nb_max ? nc : nb_max;
+    float lse2[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) lse2[h] = lse[(int64_t)b * Hq + g * G + h] * kLog2e;
+    float *row = mass + (int64_t)pair * (nb_max + 1);
+    for (int j = threadIdx.x; j <= nb_max; j += blockDim.x) {
+        const int u = j < nc ? j : (j == nb_max && tail ? nc : -1);  // slot nb_max holds the tail
+        float m = 0.f;
+        if (u >= 0) {
+            const float *x = blk_lse + ((int64_t)pair * (nb_max + 1) + u) * G * 4;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float w0 = x[h * 4], w1 = x[h * 4 + 1], w2 = x[h * 4 + 2], w3 = x[h * 4 + 3];
+                const float mx = fmaxf(fmaxf(w0, w1), fmaxf(w2, w3));
+                if (mx == -INFINITY || lse2[h] == -INFINITY) continue;
+                const float t = mx + log2f(exp2f(w0 - mx) + exp2f(w1 - mx) + exp2f(w2 - mx) + exp2f(w3 - mx));
+                m += exp2f(t - lse2[h]);
+            }
+            m *= 1.0f / (float)G;
+        }
+        row[j] = m;
+    }
+}
+
+template <int D, int BS, int G>
+static int launch_block_mass(const DecodeArgs &a, int B, const int32_t *seqlens, int block_size, int nb_max,
+                             float *mass, hipStream_t stream) {
+    dim3 grid(a.num_splits, a.Hkv, B);
+    block_mass_split_kernel<D, BS, G><<<grid, 256, 0, stream>>>(a);
+    int st = launch_status();
+    if (st != SEER_OK) return st;
+    if (a.num_splits > 1) {
+        sparse_decode_merge_kernel<D><<<dim3(B * a.Hq), 128, 0, stream>>>(a.part_o, a.part_ml, a.num_splits, a.out,
+                                                                         a.out_dtype, a.lse);
+        if ((st = launch_status()) != SEER_OK) return st;
+    }
+    block_mass_kernel<G><<<dim3(B * a.Hkv), 256, 0, stream>>>(a.blk_lse, a.lse, seqlens, a.Hq, a.Hkv, a.kv_capacity,
+                                                              block_size, nb_max, mass);
+    return launch_status();
+}
+
+template <int D, int BS>
+static int dispatch_block_mass(const DecodeArgs &a, int B, int G, const int32_t *seqlens, int block_size, int nb_max,
+                               float *mass, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_block_mass<D, BS, 1>(a, B, seqlens, block_size, nb_max, mass, stream);
+        case 2: return launch_block_mass<D, BS, 2>(a, B, seqlens, block_size, nb_max, mass, stream);
+        case 4: return launch_block_mass<D, BS, 4>(a, B, seqlens, block_size, nb_max, mass, stream);
+        case 8: return launch_block_mass<D, BS, 8>(a, B, seqlens, block_size, nb_max, mass, stream);
+    }
+    return SEER_ERR_UNSUPPORTED;
+}
+
 template <int D, int BS>
 static int dispatch_group(const DecodeArgs &a, int B, int G, hipStream_t stream) {
     switch (G) {
@@ -128,6 +201,65 @@ extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h
     a.part_o = static_cast<float *>(workspace);
     a.part_ml = S > 1 ? reinterpret_cast<float2 *>(static_cast<float *>(workspace) + (size_t)B * Hq * S * d) : nullptr;
     a.out = out; a.out_dtype = out_dtype; a.lse = lse;
+    a.blk_lse = nullptr; a.units_max = 0;
     if (d == 128) return block_size == 128 ? dispatch_group<128, 128>(a, B, G, stream) : dispatch_group<128, 64>(a, B, G, stream);
     return block_size == 128 ? dispatch_group<64, 128>(a, B, G, stream) : dispatch_group<64, 64>(a, B, G, stream);
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+extern "C" size_t seer_decode_block_mass_workspace_size(int B, int Hq, int Hkv, int d, int nb_max, int block_size,
+                                                        int num_splits) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || nb_max < 0 || Hq % Hkv != 0) return 0;
+    const int S = seer_sparse_decode_num_splits(B, Hkv, nb_max, block_size, num_splits);
+    const size_t parts = align256(seer_sparse_decode_workspace_size(B, Hq, Hkv, d, nb_max, block_size, S));
+    const size_t lse = align256((size_t)B * Hq * sizeof(float));
+    const size_t blk = (size_t)B * Hq * ((size_t)nb_max + 1) * 4 * sizeof(float);
+    return parts + lse + blk;
+}
+
+extern "C" int seer_decode_block_mass(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
+                                      const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                                      int kv_capacity, const int32_t *seqlens, int B, int Hq, int Hkv, int d,
+                                      int block_size, float softmax_scale, int nb_max, int num_splits,
+                                      void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                                      float *mass, hipStream_t stream) {
+    if (!q || !k || !v || !seqlens || !out || !mass || !workspace) return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || nb_max < 0 || kv_capacity < 0 || num_splits < 0)
+        return SEER_ERR_INVALID_ARG;
+    if (out_dtype != SEER_OUT_BF16 && out_dtype != SEER_OUT_F32) return SEER_ERR_INVALID_ARG;
+    if (skv_t < d || !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !rows_aligned16(k, skv_t) ||
+        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !(softmax_scale == softmax_scale) ||
+        !aligned16(workspace))
+        return SEER_ERR_INVALID_ARG;
+    const int G = Hq / Hkv;
+    if ((d != 64 && d != 128) || (block_size != 64 && block_size != 128) || !pow2_group(G) || G > 8)
+        return SEER_ERR_UNSUPPORTED;
+    if ((int64_t)kv_capacity * skv_t * 2 > 0x7fffffffLL) return SEER_ERR_UNSUPPORTED;
+    const int S = seer_sparse_decode_num_splits(B, Hkv, nb_max, block_size, num_splits);
+    if (S > kMaxSplits) return SEER_ERR_INVALID_ARG;
+    if (workspace_bytes < seer_decode_block_mass_workspace_size(B, Hq, Hkv, d, nb_max, block_size, S))
+        return SEER_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const size_t parts = align256(seer_sparse_decode_workspace_size(B, Hq, Hkv, d, nb_max, block_size, S));
+    const size_t lse_bytes = align256((size_t)B * Hq * sizeof(float));
+
+    DecodeArgs a;
+    a.q = q; a.sq_b = sq_b; a.sq_h = sq_h;
+    a.k = k; a.v = v; a.skv_b = skv_b; a.skv_h = skv_h; a.skv_t = skv_t;
+    a.kv_capacity = kv_capacity;
+    a.seqlens = seqlens; a.block_idx = nullptr; a.n_sel = nullptr;
+    a.k_max = nb_max; a.Hq = Hq; a.Hkv = Hkv; a.num_splits = S;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.part_o = S > 1 ? reinterpret_cast<float *>(ws) : nullptr;
+    a.part_ml = S > 1 ? reinterpret_cast<float2 *>(reinterpret_cast<float *>(ws) + (size_t)B * Hq * S * d) : nullptr;
+    a.out = out; a.out_dtype = out_dtype;
+    a.lse = lse ? lse : reinterpret_cast<float *>(ws + parts);
+    a.blk_lse = reinterpret_cast<float *>(ws + parts + lse_bytes);
+    a.units_max = nb_max + 1;
+    if (d == 128)
+        return block_size == 128 ? dispatch_block_mass<128, 128>(a, B, G, seqlens, block_size, nb_max, mass, stream)
+                                 : dispatch_block_mass<128, 64>(a, B, G, seqlens, block_size, nb_max, mass, stream);
+    return block_size == 128 ? dispatch_block_mass<64, 128>(a, B, G, seqlens, block_size, nb_max, mass, stream)
+                             : dispatch_block_mass<64, 64>(a, B, G, seqlens, block_size, nb_max, mass, stream);
 }

@@ -55,6 +55,10 @@ struct DecodeArgs {
     void *out;
     int out_dtype;
     float *lse;
+    // Ground-truth form only: per (b, KV head, unit, head, wave) log2 of the
+    // wave's sum of exp over the unit's tokens, at a stride of units_max units.
+    float *blk_lse;
+    int units_max;
 };
 
 template <int D, int BS, int G>
@@ -98,7 +102,9 @@ struct DecodeSmem {
 // One split of one (b, KV head g): attention of the group's query heads over
 // its units.  Writes the split's (o, m, l) through Mem, or with a single split
 // the normalised output.  Every thread of the 256-thread workgroup calls it.
-template <int D, int BS, int G, class Mem>
+// GT (the ground-truth form): every complete block is a unit (up to k_max of
+// them, in order) and each unit's per-wave log-sum-exp goes to a.blk_lse.
+template <int D, int BS, int G, class Mem, bool GT = false>
 __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split, int g, int b,
                                                   DecodeSmem<D, BS, G> &sm) {
     using C = DecodeCfg<D, BS, G>;
@@ -113,8 +119,8 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     int L = a.seqlens[b];
     L = L < 0 ? 0 : (L > a.kv_capacity ? a.kv_capacity : L);
     const int nc = L / BS, tail = L - nc * BS;
-    int nsel = Mem::ldi(a.n_sel + b * a.Hkv + g);
     const int kcap = a.k_max < nc ? a.k_max : nc;
+    int nsel = GT ? kcap : Mem::ldi(a.n_sel + b * a.Hkv + g);
     nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
     const int units = nsel + (tail > 0 ? 1 : 0);
     const int u0 = (int)(((int64_t)split * units) / a.num_splits);
@@ -144,7 +150,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     const uint32_t region = (uint32_t)((int64_t)a.kv_capacity * a.skv_t * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, kBufferFlags);
-    const int32_t *sel = a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
+    const int32_t *sel = GT ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
     const int wt0 = wave * C::TPW;  // first token of this wave inside a unit
     uint32_t koff[C::TPL][C::CPL], voff[C::TPLV];
 #pragma unroll
@@ -159,12 +165,15 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     for (int u = u0; u < u1; ++u) {
         int tok0, cnt;
         if (u < nsel) {
-            if (u - id0 >= 64) {
-                id0 = u;
-                ids = u + lane < nsel ? Mem::ldi(sel + u + lane) : 0;
+            int blk = u;
+            if constexpr (!GT) {
+                if (u - id0 >= 64) {
+                    id0 = u;
+                    ids = u + lane < nsel ? Mem::ldi(sel + u + lane) : 0;
+                }
+                blk = __builtin_amdgcn_readlane(ids, u - id0);
+                blk = blk < 0 ? 0 : (blk >= nc ? nc - 1 : blk);
             }
-            int blk = __builtin_amdgcn_readlane(ids, u - id0);
-            blk = blk < 0 ? 0 : (blk >= nc ? nc - 1 : blk);
             tok0 = blk * BS;
             cnt = BS;
         } else {
@@ -228,6 +237,12 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
                 lsum += s[t][h];
             }
             l_part[h] = l_part[h] * alpha[h] + lsum;
+            if constexpr (GT) {  // this wave's log2-sum-exp of the unit (its quarter of the tokens)
+                const float lw = cross_group_sum<C::LPR>(lsum);
+                if (lane == 0)
+                    a.blk_lse[(((int64_t)(b * a.Hkv + g) * a.units_max + u) * G + h) * C::NW + wave] =
+                        lw > 0.f ? m_ref + log2f(lw) : -INFINITY;
+            }
         }
 
         // Probabilities to LDS (one writer per key row), then back in the PV layout.

@@ -208,6 +208,7 @@ extern "C" int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, 
     a.part_o = S > 1 ? reinterpret_cast<float *>(ws + step_ctl_bytes(pairs)) : nullptr;
     a.part_ml = S > 1 ? reinterpret_cast<float2 *>(a.part_o + (size_t)B * Hq * S * d) : nullptr;
     a.out = out; a.out_dtype = out_dtype; a.lse = lse;
+    a.blk_lse = nullptr; a.units_max = 0;
     s.pairs = pairs;
     s.chunks = (nb_max + rpb - 1) / rpb;
     s.k_max = k_max;

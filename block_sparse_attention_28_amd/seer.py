@@ -34,6 +34,9 @@ SIGNATURES = {
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
+    "seer_decode_block_mass_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "seer_decode_block_mass": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _I, _I, _I, _I, _I, _F, _I,
+                                    _I, _P, _SZ, _P, _I, _P, _P, _P]),
     "seer_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_decode_step": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _F, _P, _I, _I, _I, _I,
                               _I, _I, _I, _F, _I, _P, _P, _P, _P, _SZ, _P, _I, _P, _P]),
@@ -192,6 +195,29 @@ def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, soft
         k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
         block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
         _ptr(lse), _stream(stream), bind=bind)
+
+
+def seer_decode_block_mass_workspace_size(B: int, Hq: int, Hkv: int, d: int, nb_max: int, block_size: int,
+                                          num_splits: int = 0) -> int:
+    return load().seer_decode_block_mass_workspace_size(B, Hq, Hkv, d, nb_max, block_size, num_splits)
+
+
+def seer_decode_block_mass(q, k, v, seqlens, block_size: int, softmax_scale: float, mass, out, lse=None,
+                           workspace=None, num_splits: int = 0, stream=None, bind: bool = False):
+    """Dense attention of q over the whole context of k/v [B, Hkv, cap, d] into out, and the group-mean
+    attention mass of every block into mass [B, Hkv, nb_max + 1] (last slot: the tail)."""
+    _bits(q), _bits(k), _bits(v)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    assert k.stride() == v.stride() and out.is_contiguous() and mass.is_contiguous()
+    assert mass.dtype == torch.float32 and mass.shape[:2] == (B, Hkv)
+    nb_max = mass.shape[2] - 1
+    out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return _call(
+        "seer_decode_block_mass", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        k.stride(2), cap, _ptr(seqlens), B, Hq, Hkv, d, block_size, float(softmax_scale), nb_max, int(num_splits),
+        _ptr(workspace), ws_bytes, _ptr(out), out_dtype, _ptr(lse), _ptr(mass), _stream(stream), bind=bind)
 
 
 def seer_block_sparse_prefill_kmax_row(L: int, block_size: int, keep_num: int, keep_den: int) -> int:

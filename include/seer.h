@@ -167,6 +167,34 @@ int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                        void *out, int out_dtype, float *lse, hipStream_t stream);
 
 /*
+ * Block-level ground truth of decoding attention ("SeerAttention: Learning
+ * Intrinsic Sparse Attention in Your LLMs", abstract v2: the block-level
+ * ground truth of the attention map, extracted next to the attention itself;
+ * the gate is distilled toward it).  Dense attention of every query head over
+ * its whole context [0, seqlens[b]) -- out and lse as seer_sparse_decode with
+ * every complete block kept -- and per (b, g) the attention mass of each block,
+ * averaged over g's query heads:
+ *   mass[b][g][j]      = (1/G) sum_h sum_{t in block j} softmax_t      j < nc_b
+ *   mass[b][g][nb_max] = the same sum over the tail [nc_b*bs, seqlens[b])
+ *   mass[b][g][j]      = 0 for nc_b <= j < nb_max (and the tail slot without a tail)
+ * Each row sums to 1 (0 for an empty context).  nb_max >= seqlens[b] / block_size
+ * (blocks past nb_max are not attended).
+ *   mass       fp32 [B][Hkv][nb_max + 1]
+ *   lse        fp32 [B][Hq] or NULL
+ *   workspace  >= seer_decode_block_mass_workspace_size(...) bytes (split
+ *              partials, the lse when lse is NULL, and per-block sums)
+ * Other arguments and limits as seer_sparse_decode.
+ */
+size_t seer_decode_block_mass_workspace_size(int B, int Hq, int Hkv, int d, int nb_max, int block_size,
+                                             int num_splits);
+int seer_decode_block_mass(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                           const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                           int kv_capacity, const int32_t *seqlens, int B, int Hq, int Hkv, int d,
+                           int block_size, float softmax_scale, int nb_max, int num_splits,
+                           void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                           float *mass, hipStream_t stream);
+
+/*
  * One whole decode step in a single launch: the gate scores, the token-budget
  * selection and the sparse decode with its merge -- the same results, bit for
  * bit, as seer_gate_scores + seer_select_blocks + seer_sparse_decode with the

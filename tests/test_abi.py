@@ -71,6 +71,19 @@ def test_sparse_decode_rejects_bad_arguments(lib, over, status):
     assert lib.seer_sparse_decode(*decode_args(**over)) == status
 
 
+def test_block_mass_rejects_bad_arguments(lib):
+    a = [FAKE, 32 * 128, 128, FAKE, FAKE, 8 * 1024 * 128, 1024 * 128, 128, 1024, FAKE, 2, 32, 8, 128, 64,
+         C.c_float(0.088), 16, 0, FAKE, 16, FAKE, 0, NULL, FAKE, NULL]
+    assert lib.seer_decode_block_mass(*a) == -3          # workspace too small
+    b = list(a)
+    b[23] = NULL                                         # no mass output
+    assert lib.seer_decode_block_mass(*b) == -1
+    b = list(a)
+    b[14] = 32                                           # block size
+    assert lib.seer_decode_block_mass(*b) == -2
+    assert lib.seer_decode_block_mass_workspace_size(2, 32, 8, 128, 16, 64, 1) == 256 + 2 * 32 * 17 * 4 * 4
+
+
 def test_workspace_size_matches_partials(lib):
     s = lib.seer_sparse_decode_num_splits(16, 8, 51, 128, 13)
     assert s == 13
