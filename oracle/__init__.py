@@ -51,6 +51,7 @@ def _bind(path: str):
         "so_pool_k": (I, [P, I64, I, I, I, P]),
         "so_gate_scores": (I, [P, I64, I, I, P, P, I, P, I, D, P, P]),
         "so_select_blocks": (I, [P, I, I, P]),
+        "so_select_policy": (I, [P, I, I, I, I, I, D, P]),
         "so_sparse_attention": (I, [P, I64, I, I, P, P, I64, I, I, P, I, D, P, P, P]),
         "so_decode_block_mass": (I, [P, I64, I, I, P, P, I64, I, I, D, P, P, P]),
         "so_pool_cache": (I, [P, I64, I64, I64, P, I, I, I, I, I, P]),
@@ -129,6 +130,18 @@ def select_blocks(S, k: int) -> np.ndarray:
     idx = np.full((max(k, 1),), -1, dtype=np.int32)
     n = _load().so_select_blocks(_p(S), S.shape[0], int(k), _p(idx))
     _check(n, "select_blocks")
+    return idx[:n].copy()
+
+
+POLICY_BUDGET, POLICY_RATIO, POLICY_THRESHOLD = 0, 1, 2
+
+
+def select_policy(S, policy: int, k_max: int, num: int = 1, den: int = 1, tau: float = 0.0) -> np.ndarray:
+    """Ascending ids kept by a selection policy (budget / ratio / threshold) over scores S [nc]."""
+    S = _f64(S)
+    idx = np.full((max(k_max, 1),), -1, dtype=np.int32)
+    n = _load().so_select_policy(_p(S), S.shape[0], int(policy), int(k_max), int(num), int(den), float(tau), _p(idx))
+    _check(n, "select_policy")
     return idx[:n].copy()
 
 

@@ -164,6 +164,41 @@ int so_select_blocks(const double *S, int nc, int k, int32_t *idx)
     return n;
 }
 
+/* ------------------------------------------------------------------ S1 --- */
+int so_select_policy(const double *S, int nc, int policy, int k_max, int num, int den, double tau, int32_t *idx)
+{
+    if (nc < 0 || k_max < 0 || (nc > 0 && !S))
+        return -1;
+    int k;
+    if (policy == 0) {
+        k = nc;
+    } else if (policy == 1) {
+        if (num < 0 || den <= 0)
+            return -1;
+        k = (int)(((int64_t)nc * num + den - 1) / den);
+    } else if (policy == 2) {
+        if (isnan(tau))
+            return -1;
+        double m = -INFINITY, z = 0.0;
+        for (int j = 0; j < nc; ++j)
+            if (S[j] > m)
+                m = S[j];
+        for (int j = 0; j < nc; ++j)
+            z += exp(S[j] - m);
+        k = 0;
+        for (int j = 0; j < nc; ++j)
+            if (exp(S[j] - m) / z >= tau)
+                ++k;
+    } else {
+        return -1;
+    }
+    if (k > nc)
+        k = nc;
+    if (k > k_max)
+        k = k_max;
+    return so_select_blocks(S, nc, k, idx);
+}
+
 /* ------------------------------------------------------------ D5 + D6 --- */
 /* Scaled dot-product softmax attention of each query row over the token set
  * T = (kept complete blocks) + (incomplete tail).  The tail has no pooled key

@@ -64,6 +64,16 @@ int so_gate_scores(const uint16_t *q, int64_t q_row_stride, int G, int d,
 /* D4: returns the number selected (min(k, nc)); idx ascending. */
 int so_select_blocks(const double *S, int nc, int k, int32_t *idx);
 
+/* S1, selection policies beyond the token budget (SeerAttention v2 abstract:
+ * the gate adapts to varying sparsity ratios).  The count kept, then the same
+ * rule as D4 (largest scores, ties toward the lower id, ids ascending):
+ *   policy 0 (budget)     k = min(k_max, nc)
+ *   policy 1 (ratio)      k = min(k_max, ceil(nc * num / den))
+ *   policy 2 (threshold)  k = min(k_max, #{j < nc : p_j >= tau}),
+ *                         p_j = exp(S_j - max S) / sum_i exp(S_i - max S)
+ * Returns k, or a negative value on bad arguments. */
+int so_select_policy(const double *S, int nc, int policy, int k_max, int num, int den, double tau, int32_t *idx);
+
 /* D5 + D6 for one KV head.  idx: ascending distinct complete-block ids.
  * w (nullable) receives the softmax weight of every token 0..L-1 (0 outside T).
  * An empty T gives out = 0 and lse = -inf. */

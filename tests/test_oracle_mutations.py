@@ -16,6 +16,7 @@ import oracle
 import test_oracle_attention as T_att
 import test_oracle_gate_select as T_gs
 import test_oracle_ground_truth as T_gt
+import test_oracle_policy as T_pol
 import test_oracle_pipeline as T_pipe
 
 
@@ -69,6 +70,10 @@ MUTATIONS = [
     ("tail share dropped from the ground truth", "const int t0 = j * bs, t1 = j < nc ? (j + 1) * bs : L;",
      "const int t0 = j * bs, t1 = j < nc ? (j + 1) * bs : j * bs;",
      lambda: T_gt.test_equal_keys_give_token_count_shares(300, 64)),
+    ("ratio count rounds down", "k = (int)(((int64_t)nc * num + den - 1) / den);",
+     "k = (int)(((int64_t)nc * num) / den);", lambda: T_pol.test_ratio_counts_closed_form(512, 1, 10, 52)),
+    ("threshold compared on the unnormalised weight", "if (exp(S[j] - m) / z >= tau)",
+     "if (exp(S[j] - m) >= tau)", lambda: T_pol.test_threshold_keeps_the_blocks_above_tau(64, 0.02)),
     ("prefill causal mask dropped", "for (int tt = 0; tt <= t; ++tt)", "for (int tt = 0; tt < L; ++tt)",
      lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
 ]
