@@ -42,11 +42,13 @@ struct GsSmem {
     float u_part[GsCfg<D, NT>::NW][D];
     float u[D];
     int hist[3][256];                 // radix histograms, used in rotation
+    float red[2][GsCfg<D, NT>::NW];   // threshold policy: per-wave max and sum
     int wcnt[2][2][GsCfg<D, NT>::NW];  // per-wave counts of the id sweep, double-buffered
 };
 
 struct GateSelectArgs {
     GateArgs gate;
+    SelectPolicy pol;
     int k_max;
     int32_t *block_idx;  // [pairs, k_max]
     int32_t *n_sel;      // [pairs]
@@ -188,9 +190,39 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
     }
     __syncthreads();  // keys complete
 
-    // 4. Selection: k = min(k_max, nc) blocks, ids ascending, -1 after.
+    // 4. Selection: k blocks by the policy, ids ascending, -1 after.
     const int k_max = gs.k_max;
-    const int k = k_max < nc ? k_max : nc;
+    int k = policy_count(gs.pol, nc, k_max);
+    if (gs.pol.kind == 2 && k > 0) {  // threshold: count the blocks with probability >= tau
+        float m = -INFINITY;
+        for (int j = tid; j < nc; j += NT) m = fmax_fast(m, key_to_float(keys[j]));
+        m = wave_max(m);
+        if (lane == 0) sm.red[0][wave] = m;
+        __syncthreads();
+        m = sm.red[0][0];
+#pragma unroll
+        for (int w = 1; w < C::NW; ++w) m = fmax_fast(m, sm.red[0][w]);
+        float z = 0.f;
+        for (int j = tid; j < nc; j += NT) z += expf(key_to_float(keys[j]) - m);
+        z = wave_sum(z);
+        if (lane == 0) sm.red[1][wave] = z;
+        __syncthreads();
+        z = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) z += sm.red[1][w];
+        const float bar = gs.pol.tau * z;
+        float cnt = 0.f;
+        for (int j = tid; j < nc; j += NT) cnt += expf(key_to_float(keys[j]) - m) >= bar ? 1.f : 0.f;
+        cnt = wave_sum(cnt);
+        __syncthreads();  // every wave has read red[0]
+        if (lane == 0) sm.red[0][wave] = cnt;
+        __syncthreads();
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) c += (int)sm.red[0][w];
+        c = __builtin_amdgcn_readfirstlane(c);
+        k = c < k ? c : k;
+    }
     int32_t *out = gs.block_idx + (int64_t)pair * k_max;
     if (k == nc || k == 0) {  // every complete block, or none, is kept
         for (int i = tid; i < k_max; i += NT) Mem::sti(out + i, i < k ? i : -1);

@@ -25,4 +25,8 @@ inline int launch_status() {
 
 inline bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
+struct SelectPolicy;
+// Checks a caller's selection policy (NULL: the token budget) and converts it.
+bool policy_from_host(const seer_select_policy *p, SelectPolicy *out);
+
 }  // namespace seer

@@ -44,13 +44,32 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Select the k largest of scores[0..n) (0 < k < n), write their ids ascending to
-// out[0..k); scores are read and ids written through Mem.  keys: LDS scratch of
-// n words, hist: LDS scratch of 256 words, both private to this wave.  Every
-// lane of the wave must call it.
+// How many blocks a (b, head) keeps (SeerAttention v2 abstract: varying
+// sparsity ratios; SeerAttention-R abstract: a token budget): kind 0 keeps
+// min(k_max, nc) (the token budget, k_max = budget / block size), kind 1
+// ceil(nc * num / den), kind 2 the blocks whose softmax probability over the
+// row's scores is at least tau; every kind is capped by k_max and nc.
+struct SelectPolicy {
+    int kind, num, den;
+    float tau;
+};
+
+__device__ __forceinline__ int policy_count(const SelectPolicy &p, int nc, int k_max) {
+    int64_t k = nc;
+    if (p.kind == 1) k = ((int64_t)nc * p.num + p.den - 1) / p.den;
+    k = k < nc ? k : nc;
+    k = k < k_max ? k : k_max;
+    return (int)(k < 0 ? 0 : k);
+}
+
+// Inverse of order_key (both zeros come back as +0).
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// scores[0..n) as order-preserving keys in LDS, read through Mem.
 template <class Mem>
-__device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, int k, uint32_t *keys, int *hist,
-                                                    int32_t *out, int lane) {
+__device__ __forceinline__ void wave_load_keys(const float *scores, int n, uint32_t *keys, int lane) {
     for (int base = 0; base < n; base += 64 * 8) {  // eight loads in flight per lane
         float v[8];
 #pragma unroll
@@ -64,6 +83,29 @@ __device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, 
             if (j < n) keys[j] = order_key(v[i]);
         }
     }
+    wave_lds_sync();
+}
+
+// Number of keys[0..n) whose softmax probability is at least tau, by one wave.
+__device__ __forceinline__ int wave_threshold_count(const uint32_t *keys, int n, float tau, int lane) {
+    float m = -INFINITY;
+    for (int j = lane; j < n; j += 64) m = fmax_fast(m, key_to_float(keys[j]));
+    m = wave_max(m);
+    float z = 0.f;
+    for (int j = lane; j < n; j += 64) z += expf(key_to_float(keys[j]) - m);
+    z = wave_sum(z);
+    const float bar = tau * z;
+    int c = 0;
+    for (int j = lane; j < n; j += 64) c += expf(key_to_float(keys[j]) - m) >= bar ? 1 : 0;
+    return (int)wave_sum((float)c);
+}
+
+// Select the k largest of the n keys in LDS (0 < k < n), write their ids
+// ascending to out[0..k) through Mem.  hist: LDS scratch of 256 words private
+// to this wave.  Every lane of the wave must call it.
+template <class Mem>
+__device__ __forceinline__ void wave_topk_from_keys(int n, int k, uint32_t *keys, int *hist, int32_t *out,
+                                                    int lane) {
     uint32_t prefix = 0;
     int need = k;  // keys still to take among those matching `prefix` so far
 #pragma unroll 1
@@ -122,24 +164,42 @@ __device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, 
     }
 }
 
-// Token-budget selection of one (b, head) = pair by one wave: k = min(k_max, nc)
-// blocks (ties to the lower id), ascending in block_idx[pair][0..k), -1 after,
-// and n_sel[pair] = k.
+// The k largest of scores[0..n) (0 < k < n), ids ascending, by one wave.
+template <class Mem>
+__device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, int k, uint32_t *keys, int *hist,
+                                                    int32_t *out, int lane) {
+    wave_load_keys<Mem>(scores, n, keys, lane);
+    wave_topk_from_keys<Mem>(n, k, keys, hist, out, lane);
+}
+
+// Selection of one (b, head) = pair by one wave: k blocks by the policy
+// (ties to the lower id), ascending in block_idx[pair][0..k), -1 after, and
+// n_sel[pair] = k.
 template <class Mem>
 __device__ __forceinline__ void select_pair_item(const float *scores, const int32_t *seqlens, int H, int nb_max,
                                                  int block_size, int k_max, int32_t *block_idx, int32_t *n_sel,
-                                                 int pair, uint32_t *keys, int *hist, int lane) {
+                                                 int pair, uint32_t *keys, int *hist, int lane,
+                                                 const SelectPolicy pol = SelectPolicy{0, 1, 1, 0.f}) {
     const int b = pair / H;
     int L = seqlens[b];
     L = L < 0 ? 0 : L;
     int nc = L / block_size;
     nc = nc > nb_max ? nb_max : nc;
-    const int k = k_max < nc ? k_max : nc;
+    int k = policy_count(pol, nc, k_max);
+    const float *row = scores + (int64_t)pair * nb_max;
+    bool loaded = false;
+    if (pol.kind == 2 && k > 0) {
+        wave_load_keys<Mem>(row, nc, keys, lane);
+        loaded = true;
+        const int c = wave_threshold_count(keys, nc, pol.tau, lane);
+        k = c < k ? c : k;
+    }
     int32_t *out = block_idx + (int64_t)pair * k_max;
     if (k == nc || k == 0) {  // every complete block, or none, is kept
         for (int i = lane; i < k_max; i += 64) Mem::sti(out + i, i < k ? i : -1);
     } else {
-        wave_topk_ascending<Mem>(scores + (int64_t)pair * nb_max, nc, k, keys, hist, out, lane);
+        if (!loaded) wave_load_keys<Mem>(row, nc, keys, lane);
+        wave_topk_from_keys<Mem>(nc, k, keys, hist, out, lane);
         for (int i = k + lane; i < k_max; i += 64) Mem::sti(out + i, -1);
     }
     if (lane == 0) Mem::sti(n_sel + pair, k);

@@ -20,6 +20,19 @@ _lib = None
 SEER_OK = 0
 SEER_OUT_BF16 = 0
 SEER_OUT_F32 = 1
+SEER_KPOOL_F32 = 0
+SEER_KPOOL_BF16 = 1
+SEER_SELECT_BUDGET, SEER_SELECT_RATIO, SEER_SELECT_THRESHOLD = 0, 1, 2
+
+
+class SelectPolicy(C.Structure):
+    """seer_select_policy: kind (budget / ratio / threshold), ratio_num / ratio_den, threshold."""
+    _fields_ = [("kind", C.c_int), ("ratio_num", C.c_int), ("ratio_den", C.c_int), ("threshold", C.c_float)]
+
+
+def policy(kind: str = "budget", num: int = 1, den: int = 1, tau: float = 0.0) -> SelectPolicy:
+    kinds = {"budget": SEER_SELECT_BUDGET, "ratio": SEER_SELECT_RATIO, "threshold": SEER_SELECT_THRESHOLD}
+    return SelectPolicy(kinds[kind], int(num), int(den), float(tau))
 
 # name -> (restype, argtypes); mirrors include/seer.h
 _P, _I, _I64, _F, _SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
@@ -29,6 +42,9 @@ SIGNATURES = {
     "seer_pool_k_blocks": (_I, [_P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _P]),
     "seer_gate_scores": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
     "seer_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "seer_select_blocks_ex": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "seer_gate_select_ex": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
+                                 _P, _P]),
     "seer_gate_select": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "seer_sparse_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -90,6 +106,9 @@ def _stream(stream) -> C.c_void_p:
     return C.c_void_p(s.cuda_stream)
 
 
+_BYREF = type(C.byref(C.c_int(0)))
+
+
 class Bound:
     """One library call with its arguments converted to C values once; calling the
     object launches it again (for tight step loops where the marshalling would
@@ -100,7 +119,8 @@ class Bound:
         self.name = name
         self.fn = getattr(load(), name)
         types = SIGNATURES[name][1]
-        self.args = tuple(a if a is None or isinstance(a, C._SimpleCData) else t(a) for t, a in zip(types, args))
+        keep = (C._SimpleCData, _BYREF)
+        self.args = tuple(a if a is None or isinstance(a, keep) else t(a) for t, a in zip(types, args))
 
     def __call__(self):
         st = self.fn(*self.args)
@@ -169,6 +189,40 @@ def seer_gate_select(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: flo
         _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), budget_tokens, _ptr(scores),
         _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel), _stream(stream),
         bind=bind)
+
+
+def _kpool_dtype(kpool) -> int:
+    if kpool.dtype == torch.float32:
+        return SEER_KPOOL_F32
+    if kpool.dtype == torch.bfloat16:
+        return SEER_KPOOL_BF16
+    raise TypeError(f"pooled keys must be float32 or bfloat16, got {kpool.dtype}")
+
+
+def seer_select_blocks_ex(scores, seqlens, block_size: int, k_max: int, pol: Optional[SelectPolicy], block_idx,
+                          n_sel, stream=None, bind: bool = False):
+    """Selection by a policy (budget / ratio / threshold); block_idx [B, H, k_max]."""
+    B, H, nb_max = scores.shape
+    assert scores.is_contiguous() and n_sel.is_contiguous()
+    return _call(
+        "seer_select_blocks_ex", _ptr(scores), _ptr(seqlens), B, H, nb_max, block_size, int(k_max),
+        C.byref(pol) if pol is not None else None, _ptr(block_idx) if k_max else None, _ptr(n_sel),
+        _stream(stream), bind=bind)
+
+
+def seer_gate_select_ex(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, k_max: int,
+                        pol: Optional[SelectPolicy], scores, block_idx, n_sel, stream=None, bind: bool = False):
+    """seer_gate_select with a selection policy and an fp32 or bf16 pooled-key table."""
+    _bits(q), _bits(wq), _bits(wk)
+    B, Hq, d = q.shape
+    Hkv, dg, _ = wq.shape
+    assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
+    assert n_sel.is_contiguous()
+    return _call(
+        "seer_gate_select_ex", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
+        _kpool_dtype(kpool), kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), int(k_max),
+        C.byref(pol) if pol is not None else None, _ptr(scores), _ptr(block_idx) if k_max else None, _ptr(n_sel),
+        _stream(stream), bind=bind)
 
 
 def seer_sparse_decode_num_splits(B: int, Hkv: int, k_max: int, block_size: int, num_splits: int = 0) -> int:

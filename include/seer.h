@@ -54,6 +54,29 @@ enum {
 
 enum { SEER_OUT_BF16 = 0, SEER_OUT_F32 = 1 };
 
+/* Element type of the pooled-key table. */
+enum { SEER_KPOOL_F32 = 0, SEER_KPOOL_BF16 = 1 };
+
+/*
+ * How many blocks a (b, head) keeps ("SeerAttention: Learning Intrinsic Sparse
+ * Attention in Your LLMs", abstract v2: the gate adapts to varying sparsity
+ * ratios; "SeerAttention-R", abstract: a token budget).  With nc complete
+ * blocks and the row width k_max of block_idx:
+ *   SEER_SELECT_BUDGET     k = min(k_max, nc)          (k_max = budget / block size)
+ *   SEER_SELECT_RATIO      k = min(k_max, nc, ceil(nc * ratio_num / ratio_den))
+ *   SEER_SELECT_THRESHOLD  k = min(k_max, #{j < nc : p_j >= threshold}),
+ *                          p_j = exp(S_j - max S) / sum_i exp(S_i - max S) in fp32
+ * then, as always, the k largest scores, ties toward the lower block id, ids
+ * ascending.  A NULL policy means the budget.  ratio_den > 0, ratio_num >= 0,
+ * threshold not NaN.
+ */
+enum { SEER_SELECT_BUDGET = 0, SEER_SELECT_RATIO = 1, SEER_SELECT_THRESHOLD = 2 };
+typedef struct {
+    int kind;
+    int ratio_num, ratio_den;
+    float threshold;
+} seer_select_policy;
+
 /* Human-readable name of a status code (static storage). */
 const char *seer_status_string(int status);
 
@@ -117,6 +140,10 @@ int seer_gate_scores(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
 int seer_select_blocks(const float *scores, const int32_t *seqlens, int B, int H, int nb_max,
                        int block_size, int budget_tokens, int32_t *block_idx, int32_t *n_sel,
                        hipStream_t stream);
+/* The same with a selection policy; k_max is the row width of block_idx. */
+int seer_select_blocks_ex(const float *scores, const int32_t *seqlens, int B, int H, int nb_max,
+                          int block_size, int k_max, const seer_select_policy *policy,
+                          int32_t *block_idx, int32_t *n_sel, hipStream_t stream);
 
 /*
  * Gate scores and token-budget selection together: the results of
@@ -134,6 +161,15 @@ int seer_gate_select(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                      const float *kpool, int nb_max, const int32_t *seqlens,
                      int B, int Hq, int Hkv, int d, int block_size, float gate_scale, int budget_tokens,
                      float *scores, int32_t *block_idx, int32_t *n_sel, hipStream_t stream);
+/* The same with a selection policy (k_max: row width of block_idx) and the
+ * pooled-key table's element type (SEER_KPOOL_BF16: see seer_pool_k_blocks_ex;
+ * always one launch, nb_max <= 12288). */
+int seer_gate_select_ex(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                        const seer_bf16 *wq, const seer_bf16 *wk, int dg,
+                        const void *kpool, int kpool_dtype, int nb_max, const int32_t *seqlens,
+                        int B, int Hq, int Hkv, int d, int block_size, float gate_scale,
+                        int k_max, const seer_select_policy *policy,
+                        float *scores, int32_t *block_idx, int32_t *n_sel, hipStream_t stream);
 
 /*
  * Sparse decode over the kept blocks (SeerAttention-R abstract: the sparse

@@ -84,6 +84,21 @@ def test_block_mass_rejects_bad_arguments(lib):
     assert lib.seer_decode_block_mass_workspace_size(2, 32, 8, 128, 16, 64, 1) == 256 + 2 * 32 * 17 * 4 * 4
 
 
+def test_policy_calls_reject_bad_policies(lib):
+    from block_sparse_attention_28_amd import seer
+    bad = [seer.SelectPolicy(7, 1, 1, 0.0), seer.SelectPolicy(1, 1, 0, 0.0), seer.SelectPolicy(1, -1, 3, 0.0),
+           seer.SelectPolicy(2, 1, 1, float("nan"))]
+    for p in bad:
+        assert lib.seer_select_blocks_ex(FAKE, FAKE, 2, 8, 512, 64, 64, C.byref(p), FAKE, FAKE, NULL) == -1
+        assert lib.seer_gate_select_ex(FAKE, 4096, 128, FAKE, FAKE, 128, FAKE, 0, 16, FAKE, 2, 32, 8, 128, 64,
+                                       C.c_float(0.1), 64, C.byref(p), FAKE, FAKE, FAKE, NULL) == -1
+    ok = seer.SelectPolicy(1, 1, 10, 0.0)
+    # valid policy, but an unknown pooled-key type / too many blocks for the LDS keys
+    assert lib.seer_gate_select_ex(FAKE, 4096, 128, FAKE, FAKE, 128, FAKE, 5, 16, FAKE, 2, 32, 8, 128, 64,
+                                   C.c_float(0.1), 64, C.byref(ok), FAKE, FAKE, FAKE, NULL) == -1
+    assert lib.seer_select_blocks_ex(FAKE, FAKE, 2, 8, 20000, 64, 64, C.byref(ok), FAKE, FAKE, NULL) == -2
+
+
 def test_workspace_size_matches_partials(lib):
     s = lib.seer_sparse_decode_num_splits(16, 8, 51, 128, 13)
     assert s == 13
