@@ -204,6 +204,41 @@ def ground_truth_context(w, lay, step, plan, dev):
             "note": "attention mass of the kept blocks + tail under dense attention; gate weights are random"}
 
 
+def bf16_table_context(w, lay, step, plan, dev, base_L):
+    """The gate + select step from a bf16 pooled-key table: its time and its drift from the fp32 contract."""
+    c = lay.cache
+    nb_max = lay.nb_max
+    k16 = torch.zeros((w.B, w.Hkv, nb_max, w.d), dtype=torch.bfloat16, device=dev)
+    ub, uj = pipeline.full_pool_lists(base_L, w.bs, dev)
+    seer.seer_pool_k_blocks_ex(c["k"], ub, uj, k16, w.bs)
+    sc = torch.empty((w.B, w.Hkv, nb_max), device=dev)
+    ix = torch.empty((w.B, w.Hkv, w.k_max), dtype=torch.int32, device=dev)
+    ns = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+    res = {}
+    for name, kp, out in (("fp32", lay.kpool, (plan.scores, plan.block_idx, plan.n_sel)), ("bf16", k16, (sc, ix, ns))):
+        call = seer.seer_gate_select_ex(step["q"], c["wq"], c["wk"], kp, step["seqlens"], w.bs, plan.gate_scale,
+                                        w.k_max, None, *out, bind=True)
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / 10, 2)
+    a, b = plan.block_idx.cpu(), ix.cpu()
+    overlap = sum(len(set(a[i, g].tolist()) & set(b[i, g].tolist())) for i in range(w.B) for g in range(w.Hkv))
+    overlap /= (w.B * w.Hkv * max(w.k_max, 1))
+    fin = torch.isfinite(plan.scores)
+    ref = torch.where(fin, plan.scores, torch.zeros_like(sc))
+    diff = torch.where(fin, sc - plan.scores, torch.zeros_like(sc))
+    drift = (diff.abs().amax(-1) / ref.abs().amax(-1).clamp(min=1e-30)).max().item()
+    return {"gate_select_us_fp32": res["fp32"], "gate_select_us_bf16": res["bf16"],
+            "selection_overlap": round(overlap, 4), "max_rel_score_drift": round(drift, 4),
+            "note": "kept-set overlap and score drift of a bf16 pooled-key table against the fp32 one"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -326,6 +361,7 @@ def main():
     graph_us = graph_step_us(plan, layers, steps, w, args) if args.graph_steps > 0 else None
     dense = dense_decode_us(w, layers[0], base_L, dev) if args.dense else None
     gt = ground_truth_context(w, layers[0], steps[0], plan, dev) if args.dense else None
+    b16 = bf16_table_context(w, layers[0], steps[0], plan, dev, base_L) if args.dense else None
 
     line = {
         "metric": METRIC,
@@ -357,6 +393,7 @@ def main():
                      "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
         "dense_decode": dense,
         "ground_truth": gt,
+        "bf16_pooled_keys": b16,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)

@@ -14,20 +14,20 @@ namespace seer {
 constexpr int kGsThreads = 1024;
 constexpr int kGsMaxBlocks = 12288;  // LDS keys of one pair (48 KiB) beside the static arrays
 
-template <int D, int G>
+template <int D, int G, class KT>
 __global__ __launch_bounds__(kGsThreads) void gate_select_kernel(const GateSelectArgs gs) {
     __shared__ GsSmem<D, kGsThreads> sm;
     extern __shared__ uint32_t keys[];
-    gate_select_pair<D, G, kGsThreads, LaunchMem>(gs, blockIdx.x, sm, keys);
+    gate_select_pair<D, G, kGsThreads, LaunchMem, KT>(gs, blockIdx.x, sm, keys);
 }
 
-template <int D>
+template <int D, class KT>
 static void launch_gate_select(const GateSelectArgs &gs, int G, unsigned grid, size_t lds, hipStream_t stream) {
     switch (G) {
-        case 1: gate_select_kernel<D, 1><<<grid, kGsThreads, lds, stream>>>(gs); break;
-        case 2: gate_select_kernel<D, 2><<<grid, kGsThreads, lds, stream>>>(gs); break;
-        case 4: gate_select_kernel<D, 4><<<grid, kGsThreads, lds, stream>>>(gs); break;
-        default: gate_select_kernel<D, 8><<<grid, kGsThreads, lds, stream>>>(gs); break;
+        case 1: gate_select_kernel<D, 1, KT><<<grid, kGsThreads, lds, stream>>>(gs); break;
+        case 2: gate_select_kernel<D, 2, KT><<<grid, kGsThreads, lds, stream>>>(gs); break;
+        case 4: gate_select_kernel<D, 4, KT><<<grid, kGsThreads, lds, stream>>>(gs); break;
+        default: gate_select_kernel<D, 8, KT><<<grid, kGsThreads, lds, stream>>>(gs); break;
     }
 }
 
@@ -54,8 +54,9 @@ extern "C" int seer_gate_select_ex(const seer_bf16 *q, int64_t sq_b, int64_t sq_
     if (pairs > 65535) return SEER_ERR_INVALID_ARG;
     const int G = Hq / Hkv;
     const bool group_ok = G == 1 || G == 2 || G == 4 || G == 8;
-    if (kpool_dtype == SEER_KPOOL_BF16) return SEER_ERR_UNSUPPORTED;
-    const bool one_launch = group_ok && nb_max <= kGsMaxBlocks && 4 * pairs >= device_cu_count();
+    const bool bf16 = kpool_dtype == SEER_KPOOL_BF16;
+    if (bf16 && (!group_ok || nb_max > kGsMaxBlocks)) return SEER_ERR_UNSUPPORTED;  // bf16: one launch only
+    const bool one_launch = group_ok && nb_max <= kGsMaxBlocks && (bf16 || 4 * pairs >= device_cu_count());
     if (!one_launch) {
         int st = seer_gate_scores(q, sq_b, sq_h, wq, wk, dg, static_cast<const float *>(kpool), nb_max, seqlens, B,
                                   Hq, Hkv, d, block_size, gate_scale, scores, stream);
@@ -67,10 +68,13 @@ extern "C" int seer_gate_select_ex(const seer_bf16 *q, int64_t sq_b, int64_t sq_
                                seqlens, block_size, scores},
                       pol, k_max, block_idx, n_sel};
     const size_t lds = (size_t)(nb_max > 0 ? nb_max : 1) * sizeof(uint32_t);
-    if (d == 128)
-        launch_gate_select<128>(gs, G, (unsigned)pairs, lds, stream);
-    else
-        launch_gate_select<64>(gs, G, (unsigned)pairs, lds, stream);
+    if (d == 128) {
+        if (bf16) launch_gate_select<128, uint16_t>(gs, G, (unsigned)pairs, lds, stream);
+        else launch_gate_select<128, float>(gs, G, (unsigned)pairs, lds, stream);
+    } else {
+        if (bf16) launch_gate_select<64, uint16_t>(gs, G, (unsigned)pairs, lds, stream);
+        else launch_gate_select<64, float>(gs, G, (unsigned)pairs, lds, stream);
+    }
     return launch_status();
 }
 

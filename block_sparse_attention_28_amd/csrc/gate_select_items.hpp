@@ -22,13 +22,41 @@
 
 namespace seer {
 
-template <int D, int NT, int G = 1>
+// Element type of the pooled-key table: fp32, or bf16 bits (half the bytes).
+template <class KT>
+struct KRow;
+template <>
+struct KRow<float> {
+    static constexpr int KB = 4, EPL = 4;  // bytes per element, elements per 16-byte lane load
+    __device__ static float dot(const float *u, uint4 x) {
+        float s = u[0] * __uint_as_float(x.x);
+        s = fmaf(u[1], __uint_as_float(x.y), s);
+        s = fmaf(u[2], __uint_as_float(x.z), s);
+        return fmaf(u[3], __uint_as_float(x.w), s);
+    }
+};
+template <>
+struct KRow<uint16_t> {
+    static constexpr int KB = 2, EPL = 8;
+    __device__ static float dot(const float *u, uint4 x) {
+        float s = u[0] * bf16lo(x.x);
+        s = fmaf(u[1], bf16hi(x.x), s);
+        s = fmaf(u[2], bf16lo(x.y), s);
+        s = fmaf(u[3], bf16hi(x.y), s);
+        s = fmaf(u[4], bf16lo(x.z), s);
+        s = fmaf(u[5], bf16hi(x.z), s);
+        s = fmaf(u[6], bf16lo(x.w), s);
+        return fmaf(u[7], bf16hi(x.w), s);
+    }
+};
+
+template <int D, int NT, int G = 1, class KT = float>
 struct GsCfg {
     static constexpr int NW = NT / 64;        // waves
-    static constexpr int LPR = D / 4;         // lanes per pooled-key row (4 floats each)
+    static constexpr int LPR = D * KRow<KT>::KB / 16;  // lanes per pooled-key row (16 bytes each)
     static constexpr int ROWS = NT / LPR;     // rows per workgroup-wide load
     // row loads in flight per thread (fewer where 1024 threads' registers also hold 8 query rows)
-    static constexpr int ITER = NT >= 1024 && D == 128 && G >= 8 ? 12 : 16;
+    static constexpr int ITER = NT >= 1024 && D == 128 && G >= 8 && KRow<KT>::KB == 4 ? 12 : 16;
     static constexpr int RPB = ROWS * ITER;   // rows per batch
     static constexpr int CH = D / 8;          // 16-byte bf16 chunks per weight row
     static constexpr int RG = NT / CH;        // weight-row groups
@@ -55,11 +83,12 @@ struct GateSelectArgs {
 };
 
 // Every thread of the NT-thread workgroup calls it; keys: LDS scratch of nb_max
-// words.  G query heads per KV head; dg <= 256.
-template <int D, int G, int NT, class Mem>
+// words.  G query heads per KV head; dg <= 256; KT the pooled keys' element type.
+template <int D, int G, int NT, class Mem, class KT = float>
 __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int pair, GsSmem<D, NT> &sm,
                                                  uint32_t *keys) {
-    using C = GsCfg<D, NT, G>;
+    using C = GsCfg<D, NT, G, KT>;
+    using KR = KRow<KT>;
     const GateArgs &ga = gs.gate;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -87,11 +116,12 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
     for (int i = 0; i < C::WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the u inputs first
     const int lr = tid / C::LPR, lc = tid % C::LPR;
-    const auto kprs = buffer_rsrc(ga.kpool + (int64_t)pair * nb_max * D, (uint32_t)nb_max * D * 4);
-    auto krow = [&](int j) { return (uint32_t)((j < nb_max ? j : nb_max - 1) * D * 4 + lc * 16); };
-    float4 x[C::ITER];
+    const KT *kpool = reinterpret_cast<const KT *>(ga.kpool);
+    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)nb_max * D * KR::KB);
+    auto krow = [&](int j) { return (uint32_t)((j < nb_max ? j : nb_max - 1) * D * KR::KB + lc * 16); };
+    uint4 x[C::ITER];
 #pragma unroll
-    for (int it = 0; it < C::ITER; ++it) x[it] = as_float4(buf_ld16_nt(kprs, krow(lr + it * C::ROWS), 0));
+    for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(lr + it * C::ROWS), 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. u = gate_scale * Wk^T (Wq qbar), qbar = mean of the group's query heads.
@@ -167,17 +197,20 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
     nc = __builtin_amdgcn_readfirstlane(nc);
     float *srow = ga.scores + (int64_t)pair * nb_max;
     for (int j = nc + tid; j < nb_max; j += NT) Mem::stf(srow + j, -INFINITY);
-    const float4 uu = reinterpret_cast<const float4 *>(sm.u)[lc];
+    float uu[KR::EPL];
+#pragma unroll
+    for (int e = 0; e < KR::EPL; ++e) uu[e] = sm.u[lc * KR::EPL + e];
     for (int j0 = 0;;) {
 #pragma unroll
         for (int it = 0; it < C::ITER; ++it) {
             const int j = j0 + lr + it * C::ROWS;
-            float s = uu.x * x[it].x;
-            s = fmaf(uu.y, x[it].y, s);
-            s = fmaf(uu.z, x[it].z, s);
-            s = fmaf(uu.w, x[it].w, s);
-            s = group_sum<16>(s);
-            if constexpr (C::LPR == 32) s = sum_xor16(s);
+            float s = KR::dot(uu, x[it]);
+            if constexpr (C::LPR == 8) {
+                s = group_sum<8>(s);
+            } else {
+                s = group_sum<16>(s);
+                if constexpr (C::LPR == 32) s = sum_xor16(s);
+            }
             if (lc == 0 && j < nc) {
                 Mem::stf(srow + j, s);
                 keys[j] = order_key(s);
@@ -186,7 +219,7 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
         j0 += C::RPB;
         if (j0 >= nc) break;
 #pragma unroll
-        for (int it = 0; it < C::ITER; ++it) x[it] = as_float4(buf_ld16_nt(kprs, krow(j0 + lr + it * C::ROWS), 0));
+        for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(j0 + lr + it * C::ROWS), 0);
     }
     __syncthreads();  // keys complete
 

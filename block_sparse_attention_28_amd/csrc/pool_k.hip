@@ -16,10 +16,10 @@
 
 namespace seer {
 
-template <int D, int BS>
+template <int D, int BS, class KT>
 __global__ __launch_bounds__(256) void pool_k_kernel(const uint16_t *k, int64_t sk_b, int64_t sk_h, int64_t sk_t,
                                                      int B, int Hkv, int kv_capacity, const int32_t *upd_b,
-                                                     const int32_t *upd_blk, float *kpool, int nb_max) {
+                                                     const int32_t *upd_blk, KT *kpool, int nb_max) {
     constexpr int CH = D / 8, RG = 256 / CH;  // chunks per row, row groups
     const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int b = upd_b[i], j = upd_blk[i];
@@ -46,7 +46,12 @@ __global__ __launch_bounds__(256) void pool_k_kernel(const uint16_t *k, int64_t 
         float s = 0.f;
 #pragma unroll
         for (int g = 0; g < RG; ++g) s += part[g][tid];
-        kpool[(((int64_t)b * Hkv + h) * nb_max + j) * D + tid] = s * (1.0f / BS);
+        const float mean = s * (1.0f / BS);  // exact scaling: BS is a power of two
+        const int64_t at = (((int64_t)b * Hkv + h) * nb_max + j) * D + tid;
+        if constexpr (sizeof(KT) == 4)
+            kpool[at] = mean;
+        else
+            kpool[at] = f32_to_bf16(mean);  // the bf16 table: round to nearest even
     }
 }
 
@@ -54,10 +59,12 @@ __global__ __launch_bounds__(256) void pool_k_kernel(const uint16_t *k, int64_t 
 
 using namespace seer;
 
-extern "C" int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t sk_t, int B, int Hkv,
-                                  int d, int block_size, int kv_capacity, const int32_t *upd_b,
-                                  const int32_t *upd_blk, int n_upd, float *kpool, int nb_max, hipStream_t stream) {
+extern "C" int seer_pool_k_blocks_ex(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t sk_t, int B, int Hkv,
+                                     int d, int block_size, int kv_capacity, const int32_t *upd_b,
+                                     const int32_t *upd_blk, int n_upd, void *kpool, int kpool_dtype, int nb_max,
+                                     hipStream_t stream) {
     if (n_upd < 0 || B <= 0 || Hkv <= 0 || nb_max < 0 || kv_capacity < 0) return SEER_ERR_INVALID_ARG;
+    if (kpool_dtype != SEER_KPOOL_F32 && kpool_dtype != SEER_KPOOL_BF16) return SEER_ERR_INVALID_ARG;
     if (n_upd == 0) return SEER_OK;
     if (!k || !upd_b || !upd_blk || !kpool || !rows_aligned16(k, sk_t) || sk_h % 8 || sk_b % 8 || sk_t < d ||
         !aligned16(kpool))
@@ -65,9 +72,17 @@ extern "C" int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h
     if ((d != 64 && d != 128) || (block_size != 64 && block_size != 128)) return SEER_ERR_UNSUPPORTED;
     if (Hkv > 65535) return SEER_ERR_INVALID_ARG;
     dim3 grid(n_upd, Hkv);
-#define SEER_POOL(D_, BS_)                                                                                   \
-    pool_k_kernel<D_, BS_><<<grid, 256, 0, stream>>>(k, sk_b, sk_h, sk_t, B, Hkv, kv_capacity, upd_b, upd_blk, \
-                                                     kpool, nb_max)
+    float *kp32 = static_cast<float *>(kpool);
+    uint16_t *kp16 = static_cast<uint16_t *>(kpool);
+#define SEER_POOL(D_, BS_)                                                                                           \
+    do {                                                                                                             \
+        if (kpool_dtype == SEER_KPOOL_F32)                                                                           \
+            pool_k_kernel<D_, BS_, float><<<grid, 256, 0, stream>>>(k, sk_b, sk_h, sk_t, B, Hkv, kv_capacity, upd_b, \
+                                                                    upd_blk, kp32, nb_max);                          \
+        else                                                                                                         \
+            pool_k_kernel<D_, BS_, uint16_t><<<grid, 256, 0, stream>>>(k, sk_b, sk_h, sk_t, B, Hkv, kv_capacity,     \
+                                                                       upd_b, upd_blk, kp16, nb_max);                \
+    } while (0)
     if (d == 128) {
         if (block_size == 128) SEER_POOL(128, 128); else SEER_POOL(128, 64);
     } else {
@@ -75,4 +90,11 @@ extern "C" int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h
     }
 #undef SEER_POOL
     return launch_status();
+}
+
+extern "C" int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t sk_t, int B, int Hkv,
+                                  int d, int block_size, int kv_capacity, const int32_t *upd_b,
+                                  const int32_t *upd_blk, int n_upd, float *kpool, int nb_max, hipStream_t stream) {
+    return seer_pool_k_blocks_ex(k, sk_b, sk_h, sk_t, B, Hkv, d, block_size, kv_capacity, upd_b, upd_blk, n_upd,
+                                 kpool, SEER_KPOOL_F32, nb_max, stream);
 }

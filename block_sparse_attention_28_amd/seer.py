@@ -40,6 +40,7 @@ SIGNATURES = {
     "seer_status_string": (C.c_char_p, [_I]),
     "seer_version": (_I, []),
     "seer_pool_k_blocks": (_I, [_P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _P]),
+    "seer_pool_k_blocks_ex": (_I, [_P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _I, _P]),
     "seer_gate_scores": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
     "seer_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "seer_select_blocks_ex": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
@@ -151,6 +152,18 @@ def seer_pool_k_blocks(k, upd_b, upd_blk, kpool, block_size: int, stream=None, b
     return _call(
         "seer_pool_k_blocks", _ptr(k), k.stride(0), k.stride(1), k.stride(2), B, Hkv, d, block_size, cap,
         _ptr(upd_b), _ptr(upd_blk), upd_b.numel(), _ptr(kpool), kpool.shape[2], _stream(stream), bind=bind)
+
+
+def seer_pool_k_blocks_ex(k, upd_b, upd_blk, kpool, block_size: int, stream=None, bind: bool = False):
+    """seer_pool_k_blocks into an fp32 or bf16 table (its dtype decides)."""
+    _bits(k)
+    B, Hkv, cap, d = k.shape
+    assert kpool.is_contiguous() and kpool.shape[:2] == (B, Hkv)
+    assert upd_b.dtype == torch.int32 and upd_blk.dtype == torch.int32 and upd_b.numel() == upd_blk.numel()
+    return _call(
+        "seer_pool_k_blocks_ex", _ptr(k), k.stride(0), k.stride(1), k.stride(2), B, Hkv, d, block_size, cap,
+        _ptr(upd_b), _ptr(upd_blk), upd_b.numel(), _ptr(kpool), _kpool_dtype(kpool), kpool.shape[2],
+        _stream(stream), bind=bind)
 
 
 def seer_gate_scores(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, scores, stream=None,

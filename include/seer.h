@@ -101,6 +101,12 @@ int seer_pool_k_blocks(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t s
                        int B, int Hkv, int d, int block_size, int kv_capacity,
                        const int32_t *upd_b, const int32_t *upd_blk, int n_upd,
                        float *kpool, int nb_max, hipStream_t stream);
+/* The same into an fp32 (SEER_KPOOL_F32) or bf16 (SEER_KPOOL_BF16: the fp32
+ * mean rounded to nearest even; half the gate's bytes) table [B][Hkv][nb_max][d]. */
+int seer_pool_k_blocks_ex(const seer_bf16 *k, int64_t sk_b, int64_t sk_h, int64_t sk_t,
+                          int B, int Hkv, int d, int block_size, int kv_capacity,
+                          const int32_t *upd_b, const int32_t *upd_blk, int n_upd,
+                          void *kpool, int kpool_dtype, int nb_max, hipStream_t stream);
 
 /*
  * Gate scores of one decode step (SeerAttention-R abstract: the gate keeps

@@ -141,3 +141,87 @@ def test_ratio_policy_end_to_end_decode():
             ro, rl, _ = oracle.sparse_attention(qb[g * 4:(g + 1) * 4], kb[g], vb[g], w.bs, gi[b, g, :gn[b, g]],
                                                 1 / math.sqrt(w.d), L=L)
             assert np.abs(out[b, g * 4:(g + 1) * 4].cpu().double().numpy() - ro).max() <= 1e-4
+
+
+# ---- bf16 pooled-key table (half the gate's bytes) ----
+
+def pooled_tables(w: DecodeWorkload):
+    c = inputs.decode_cache(w, "cuda")
+    cap = c["k"].shape[2]
+    nb_max = cap // w.bs
+    from block_sparse_attention_28_amd import pipeline
+    ub, uj = pipeline.full_pool_lists(c["seqlens"].cpu(), w.bs)
+    k32 = torch.zeros((w.B, w.Hkv, nb_max, w.d), dtype=torch.float32, device="cuda")
+    k16 = torch.zeros((w.B, w.Hkv, nb_max, w.d), dtype=torch.bfloat16, device="cuda")
+    seer.seer_pool_k_blocks(c["k"], ub, uj, k32, w.bs)
+    seer.seer_pool_k_blocks_ex(c["k"], ub, uj, k16, w.bs)
+    torch.cuda.synchronize()
+    return c, nb_max, k32, k16
+
+
+def test_pool_bf16_table_is_the_rounded_mean():
+    w = DecodeWorkload(name="pool16", B=2, Hq=8, Hkv=2, d=128, bs=64, budget=0, seed=81, L_range=(300, 5000))
+    c, nb_max, k32, k16 = pooled_tables(w)
+    for b in range(w.B):
+        L = int(c["seqlens"][b])
+        nc = L // w.bs
+        ref = oracle.pool_cache(host_bits(c["k"][b:b + 1]), np.array([L], np.int32), w.bs, nb_max)[0, :, :nc]
+        got = k16[b, :, :nc].float().cpu().double().numpy()
+        # a correct rounding of the mean: within half a bf16 step, with slack for the fp32 sum
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert np.all(np.abs(got - ref) <= 0.5 * step + 1e-6 * np.abs(ref) + 1e-30)
+        # and, away from rounding midpoints, exactly the nearest bf16
+        rne = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+        far = np.abs(np.abs(ref - rne) - 0.5 * step) > 1e-5 * step
+        assert np.array_equal(got[far], rne[far])
+        # the bf16 table is the fp32 table rounded to nearest even
+        assert torch.equal(k16[b, :, :nc], k32[b, :, :nc].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("name,pol", [POLICIES[0], POLICIES[2], POLICIES[5]], ids=["ratio", "threshold", "budget"])
+def test_gate_select_bf16_table(name, pol):
+    w = DecodeWorkload(name="gate16", B=16, Hq=16, Hkv=4, d=128, bs=64, budget=0, seed=82, L_range=(100, 20000))
+    c, nb_max, k32, k16 = pooled_tables(w)
+    k_max = 64
+    scores = torch.empty((w.B, w.Hkv, nb_max), device="cuda")
+    idx = torch.full((w.B, w.Hkv, k_max), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((w.B, w.Hkv), -7, dtype=torch.int32, device="cuda")
+    q = inputs.decode_query(w, 0, "cuda")
+    gscale = 1 / math.sqrt(w.d)
+    seer.seer_gate_select_ex(q, c["wq"], c["wk"], k16, c["seqlens"], w.bs, gscale, k_max, pol, scores, idx, n_sel)
+    torch.cuda.synchronize()
+    seqlens = c["seqlens"].cpu()
+    check_rows(scores, seqlens, w.bs, nb_max, k_max, pol, idx, n_sel)
+    qh, wq, wk = host_bits(q), host_bits(c["wq"]), host_bits(c["wk"])
+    for b in (0, w.B - 1):
+        nc = int(seqlens[b]) // w.bs
+        for g in range(w.Hkv):
+            kp = k16[b, g, :nc].float().cpu().double().numpy()   # the oracle gate on the same bf16 table
+            _, S = oracle.gate_scores(qh[b, g * 4:(g + 1) * 4], wq[g], wk[g], kp, gscale)
+            rel = np.abs(scores[b, g, :nc].cpu().double().numpy() - S).max() / np.abs(S).max()
+            assert rel <= 1e-4
+
+
+def test_bf16_table_ranking_drift_against_fp32():
+    """Budget selection from the bf16 table against the fp32 contract, 64 (b, KV head) pairs, 512 blocks."""
+    w = DecodeWorkload(name="drift16", B=8, Hq=32, Hkv=8, d=128, bs=128, budget=6553, seed=83, L=65536,
+                       shifted_frac=0.05, shift=2.0)
+    c, nb_max, k32, k16 = pooled_tables(w)
+    q = inputs.decode_query(w, 0, "cuda")
+    gscale = 1 / math.sqrt(w.d)
+    res = []
+    for kp in (k32, k16):
+        sc = torch.empty((w.B, w.Hkv, nb_max), device="cuda")
+        ix = torch.empty((w.B, w.Hkv, w.k_max), dtype=torch.int32, device="cuda")
+        ns = torch.empty((w.B, w.Hkv), dtype=torch.int32, device="cuda")
+        seer.seer_gate_select_ex(q, c["wq"], c["wk"], kp, c["seqlens"], w.bs, gscale, w.k_max, None, sc, ix, ns)
+        res.append((sc, ix))
+    torch.cuda.synchronize()
+    (s32, i32), (s16, i16) = res
+    overlap = np.mean([len(set(i32[b, g].tolist()) & set(i16[b, g].tolist())) / w.k_max
+                       for b in range(w.B) for g in range(w.Hkv)])
+    drift = ((s16 - s32).abs().amax(-1) / s32.abs().amax(-1)).max().item()
+    say(f"  bf16 table: selection overlap {overlap:.4f}, max relative score drift {drift:.2e}")
+    # rounding the pooled keys to bf16 (a 2^-9 relative step; the mean-shifted blocks, pooled near 2.0,
+    # lose the most) moves scores by up to a few percent of the row's largest, yet the kept sets agree
+    assert overlap >= 0.95 and drift < 0.2
