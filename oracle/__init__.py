@@ -57,6 +57,8 @@ def _bind(path: str):
         "so_pool_cache": (I, [P, I64, I64, I64, P, I, I, I, I, I, P]),
         "so_decode_step": (I, [P, I64, I64, P, P, I64, I64, I64, P, I, I, I, I, I, I,
                                P, P, I, D, P, I, D, P, P, P, P, P]),
+        "so_decode_step_per_head": (I, [P, I64, I64, P, P, I64, I64, I64, P, I, I, I, I, I, I,
+                                        P, P, I, D, P, I, D, P, P, P, P, P]),
         "so_prefill_gate": (I, [P, P, I64, I, I, I, P, P, I, D, I, I, P, P, P, I]),
         "so_prefill_attention": (I, [P, P, P, I64, I, I, I, P, P, I, D, I, I, P, P]),
         "so_prefill": (I, [P, P, P, I, I, I, I, I, P, P, I, D, I, I, P, P, I, D, I, I, P, P]),
@@ -213,6 +215,28 @@ def decode_step(q, k, v, seqlens, bs: int, budget: int, wq, wk, gate_scale: floa
                                   _p(seqlens), B, Hq, Hkv, d, bs, int(budget), _p(wq), _p(wk), dg,
                                   float(gate_scale), _p(kpool), nb_max, float(softmax_scale),
                                   _p(scores), _p(idx), _p(n_sel), _p(out), _p(lse)), "decode_step")
+    return {"scores": scores, "idx": idx[:, :, :kmax], "n_sel": n_sel, "out": out, "lse": lse}
+
+
+def decode_step_per_head(q, k, v, seqlens, bs: int, budget: int, wq, wk, gate_scale: float, kpool,
+                         softmax_scale: float) -> dict:
+    """decode_step with per-query-head selection: scores, idx, n_sel per query head."""
+    q, k, v, wq, wk = _u16(q), _u16(k), _u16(v), _u16(wq), _u16(wk)
+    seqlens, kpool = _i32(seqlens), _f64(kpool)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    dg = wq.shape[1]
+    nb_max = kpool.shape[2]
+    kmax = budget // bs
+    scores = np.zeros((B, Hq, nb_max), dtype=np.float64)
+    idx = np.full((B, Hq, max(kmax, 1)), -1, dtype=np.int32)
+    n_sel = np.zeros((B, Hq), dtype=np.int32)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    _check(_load().so_decode_step_per_head(_p(q), Hq * d, d, _p(k), _p(v), Hkv * cap * d, cap * d, d,
+                                           _p(seqlens), B, Hq, Hkv, d, bs, int(budget), _p(wq), _p(wk), dg,
+                                           float(gate_scale), _p(kpool), nb_max, float(softmax_scale),
+                                           _p(scores), _p(idx), _p(n_sel), _p(out), _p(lse)), "decode_step_per_head")
     return {"scores": scores, "idx": idx[:, :, :kmax], "n_sel": n_sel, "out": out, "lse": lse}
 
 

@@ -375,6 +375,58 @@ int so_decode_step(const uint16_t *q, int64_t sq_b, int64_t sq_h,
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------ V1 --- */
+int so_decode_step_per_head(const uint16_t *q, int64_t sq_b, int64_t sq_h,
+                            const uint16_t *k, const uint16_t *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                            const int32_t *seqlens, int B, int Hq, int Hkv, int d, int bs, int budget,
+                            const uint16_t *wq, const uint16_t *wk, int dg, double gate_scale,
+                            const double *kpool, int nb_max, double softmax_scale,
+                            double *scores, int32_t *idx, int32_t *n_sel, double *out, double *lse)
+{
+    if (!q || !k || !v || !seqlens || !wq || !wk || !kpool || !idx || !n_sel || !out || !lse ||
+        B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || d <= 0 || bs <= 0 || budget < 0 || dg <= 0)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] / bs > nb_max)
+            return -1;
+    int G = Hq / Hkv, kmax = budget / bs, bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (int p = 0; p < B * Hkv; ++p) {
+        int b = p / Hkv, g = p % Hkv, L = seqlens[b], nc = L / bs;
+        const uint16_t *qg = q + b * sq_b + (int64_t)g * G * sq_h;
+        double *sh = (double *)malloc(sizeof(double) * (size_t)G * (size_t)(nc > 0 ? nc : 1));
+        double *S = (double *)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
+        if (!sh || !S) {
+            free(sh);
+            free(S);
+            bad = 1;
+            continue;
+        }
+        /* D2 per head (the group mean S is not used) */
+        bad |= so_gate_scores(qg, sq_h, G, d, wq + (int64_t)g * dg * d, wk + (int64_t)g * dg * d, dg,
+                              kpool + ((int64_t)b * Hkv + g) * nb_max * d, nc, gate_scale, sh, S) != 0;
+        for (int h = 0; h < G; ++h) {
+            const int64_t row = (int64_t)b * Hq + (int64_t)g * G + h;
+            if (scores)
+                for (int j = 0; j < nb_max; ++j)
+                    scores[row * nb_max + j] = j < nc ? sh[(int64_t)h * nc + j] : -INFINITY;
+            int32_t *sel = idx + row * kmax;
+            for (int i = 0; i < kmax; ++i)
+                sel[i] = -1;
+            int n = so_select_blocks(sh + (int64_t)h * nc, nc, kmax, sel);
+            bad |= n < 0;
+            n_sel[row] = n < 0 ? 0 : n;
+            if (n >= 0)
+                bad |= so_sparse_attention(qg + h * sq_h, sq_h, 1, d, k + b * skv_b + g * skv_h,
+                                           v + b * skv_b + g * skv_h, skv_t, L, bs, sel, n, softmax_scale,
+                                           out + row * d, lse + row, NULL) != 0;
+        }
+        free(sh);
+        free(S);
+    }
+    return bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------------ prefill --- */
 /* k_i = ceil((i + 1) * num / den) in integers, kept within [1, i + 1]. */
 static int keep_count(int i, int keep_num, int keep_den)

@@ -19,6 +19,7 @@
  *         ties toward the lower block index, emitted in ascending order
  *     D5  token set T = kept blocks plus the incomplete tail [nc*bs, L)
  *     D6  softmax attention of every query head over T
+ *     V1  variant: every query head selects its own blocks by its own s_hj
  *     G1  ground truth: attention mass of every block under dense attention,
  *         averaged over the group's query heads
  *   prefill, per head
@@ -108,6 +109,18 @@ int so_decode_step(const uint16_t *q, int64_t sq_b, int64_t sq_h,
                    const uint16_t *wq, const uint16_t *wk, int dg, double gate_scale,
                    const double *kpool, int nb_max, double softmax_scale,
                    double *scores, int32_t *idx, int32_t *n_sel, double *out, double *lse);
+
+/* V1, per-query-head selection (the alternative to D3's shared group
+ * selection): every query head keeps its own k = min(budget / bs, nc) blocks
+ * by its own gate score s_hj (D2, no group mean) and attends only those (plus
+ * the tail).  scores [B][Hq][nb_max] (nullable; -inf past nc), idx
+ * [B][Hq][budget/bs] padded with -1, n_sel [B][Hq], out [B][Hq][d], lse [B][Hq]. */
+int so_decode_step_per_head(const uint16_t *q, int64_t sq_b, int64_t sq_h,
+                            const uint16_t *k, const uint16_t *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                            const int32_t *seqlens, int B, int Hq, int Hkv, int d, int bs, int budget,
+                            const uint16_t *wq, const uint16_t *wk, int dg, double gate_scale,
+                            const double *kpool, int nb_max, double softmax_scale,
+                            double *scores, int32_t *idx, int32_t *n_sel, double *out, double *lse);
 
 /* P1..P3 for one head.  nb = ceil(L / bs); S (nullable) [nb][nb], -inf above the diagonal.
  * kv_blocks [nb][kmax_row] ascending, padded with -1; kv_count [nb]. */

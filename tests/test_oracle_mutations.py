@@ -17,6 +17,7 @@ import test_oracle_attention as T_att
 import test_oracle_gate_select as T_gs
 import test_oracle_ground_truth as T_gt
 import test_oracle_policy as T_pol
+import test_oracle_per_head as T_ph
 import test_oracle_pipeline as T_pipe
 
 
@@ -74,6 +75,8 @@ MUTATIONS = [
      "k = (int)(((int64_t)nc * num) / den);", lambda: T_pol.test_ratio_counts_closed_form(512, 1, 10, 52)),
     ("threshold compared on the unnormalised weight", "if (exp(S[j] - m) / z >= tau)",
      "if (exp(S[j] - m) >= tau)", lambda: T_pol.test_threshold_keeps_the_blocks_above_tau(64, 0.02)),
+    ("per-head variant selects from the group mean", "int n = so_select_blocks(sh + (int64_t)h * nc, nc, kmax, sel);",
+     "int n = so_select_blocks(S, nc, kmax, sel);", T_ph.test_heads_differ_and_each_head_is_its_own_masked_attention),
     ("prefill causal mask dropped", "for (int tt = 0; tt <= t; ++tt)", "for (int tt = 0; tt < L; ++tt)",
      lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
 ]
