@@ -239,6 +239,47 @@ def bf16_table_context(w, lay, step, plan, dev, base_L):
             "note": "kept-set overlap and score drift of a bf16 pooled-key table against the fp32 one"}
 
 
+def per_head_context(w, lay, step, plan, dev):
+    """Per-query-head selection on the first step: gate + per-head select, union decode; bytes against shared."""
+    c = lay.cache
+    nb_max = lay.nb_max
+    sc = torch.empty((w.B, w.Hq, nb_max), device=dev)
+    ix = torch.empty((w.B, w.Hq, w.k_max), dtype=torch.int32, device=dev)
+    ns = torch.empty((w.B, w.Hq), dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    wsb = seer.seer_sparse_decode_heads_workspace_size(w.B, w.Hq, w.Hkv, w.d, w.k_max, nb_max, w.bs, 0)
+    ws = torch.zeros((wsb + 3) // 4 + 4, dtype=torch.float32, device=dev)
+    gate = seer.seer_gate_select_heads(step["q"], c["wq"], c["wk"], lay.kpool, step["seqlens"], w.bs,
+                                       plan.gate_scale, w.budget, sc, ix, ns, bind=True)
+    dec = seer.seer_sparse_decode_heads(step["q"], c["k"], c["v"], step["seqlens"], ix, ns, nb_max, w.bs,
+                                        plan.softmax_scale, out, lse, ws, bind=True)
+    gate()
+    dec()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    n = 10
+    t_gate = t_dec = 0.0
+    for _ in range(n):
+        ev[0].record()
+        gate()
+        ev[1].record()
+        dec()
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_gate += ev[0].elapsed_time(ev[1]) * 1e3 / n
+        t_dec += ev[1].elapsed_time(ev[2]) * 1e3 / n
+    idx = ix.cpu().view(w.B, w.Hkv, w.G * w.k_max)
+    union = sum(len(set(idx[b, g].tolist()) - {-1}) for b in range(w.B) for g in range(w.Hkv))
+    shared = int(plan.n_sel.sum().item())
+    kv = sum(w.Hkv * (L % w.bs) for L in step["L"]) + union * w.bs   # tokens read: union blocks + tails
+    kv_bytes = kv * w.d * 2 * 2
+    return {"gate_select_heads_us": round(t_gate, 2), "decode_heads_us": round(t_dec, 2),
+            "union_blocks_over_shared": round(union / max(shared, 1), 3),
+            "decode_effective_GBps": round(kv_bytes / (t_dec * 1e-6) / 1e9, 1),
+            "note": "every query head keeps its own blocks; the decode reads each group's union once"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -362,6 +403,7 @@ def main():
     dense = dense_decode_us(w, layers[0], base_L, dev) if args.dense else None
     gt = ground_truth_context(w, layers[0], steps[0], plan, dev) if args.dense else None
     b16 = bf16_table_context(w, layers[0], steps[0], plan, dev, base_L) if args.dense else None
+    ph = per_head_context(w, layers[0], steps[0], plan, dev) if args.dense else None
 
     line = {
         "metric": METRIC,
@@ -394,6 +436,7 @@ def main():
         "dense_decode": dense,
         "ground_truth": gt,
         "bf16_pooled_keys": b16,
+        "per_head_selection": ph,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)

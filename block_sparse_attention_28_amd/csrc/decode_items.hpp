@@ -36,6 +36,7 @@
 
 #include "seer_device.hpp"
 #include "seer_host.hpp"
+#include "topk_wave.hpp"
 
 #include <math.h>
 
@@ -57,9 +58,20 @@ struct DecodeArgs {
     float *lse;
     // Ground-truth form only: per (b, KV head, unit, head, wave) log2 of the
     // wave's sum of exp over the unit's tokens, at a stride of units_max units.
+    // Per-head form: units_max is the pooled-table width nb_max.
     float *blk_lse;
     int units_max;
 };
+
+// Per-head form: LDS words the union of a group's block sets needs (bitmaps,
+// ascending union ids, per-id head masks).
+__host__ __device__ inline int heads_union_cap(int nb_max, int G, int k_max) {
+    const int64_t c = (int64_t)G * k_max;
+    return (int)(c < nb_max ? c : nb_max);
+}
+__host__ __device__ inline int heads_union_words(int nb_max, int G, int k_max) {
+    return G * ((nb_max + 31) / 32) + 2 * heads_union_cap(nb_max, G, k_max);
+}
 
 template <int D, int BS, int G>
 struct DecodeCfg {
@@ -97,6 +109,7 @@ struct DecodeSmem {
     float p[C::NW][C::TPW][G];
     float o[C::NW][G][D];
     float m[C::NW][G], l[C::NW][G];
+    int n_union;  // per-head form: size of the group's union of kept blocks
 };
 
 // One split of one (b, KV head g): attention of the group's query heads over
@@ -104,9 +117,12 @@ struct DecodeSmem {
 // the normalised output.  Every thread of the 256-thread workgroup calls it.
 // GT (the ground-truth form): every complete block is a unit (up to k_max of
 // them, in order) and each unit's per-wave log-sum-exp goes to a.blk_lse.
-template <int D, int BS, int G, class Mem, bool GT = false>
+// PH (the per-head form): block_idx / n_sel hold one set per query head; the
+// units are the union of the group's sets, ascending, and a head gives no
+// weight to a unit it did not keep (dyn: heads_union_words(...) LDS words).
+template <int D, int BS, int G, class Mem, bool GT = false, bool PH = false>
 __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split, int g, int b,
-                                                  DecodeSmem<D, BS, G> &sm) {
+                                                  DecodeSmem<D, BS, G> &sm, uint32_t *dyn = nullptr) {
     using C = DecodeCfg<D, BS, G>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / C::LPR, c = lane % C::LPR;      // QK layout
@@ -120,8 +136,62 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     L = L < 0 ? 0 : (L > a.kv_capacity ? a.kv_capacity : L);
     const int nc = L / BS, tail = L - nc * BS;
     const int kcap = a.k_max < nc ? a.k_max : nc;
-    int nsel = GT ? kcap : Mem::ldi(a.n_sel + b * a.Hkv + g);
-    nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
+    int nsel = 0;
+    uint32_t *uid = nullptr, *umask = nullptr;
+    if constexpr (PH) {
+        // Union of the G heads' sets: one bitmap per head, then wave 0 lists the
+        // set bits in ascending order with the mask of the heads that kept each.
+        const int nb_max = a.units_max, W = (nb_max + 31) / 32;
+        uint32_t *bm = dyn;
+        uid = dyn + G * W;
+        umask = uid + heads_union_cap(nb_max, G, a.k_max);
+        for (int i = tid; i < G * W; i += C::NT) bm[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < G * a.k_max; i += C::NT) {
+            const int h = i / a.k_max, r = i % a.k_max;
+            const int64_t row = (int64_t)b * a.Hq + g * G + h;
+            int n = Mem::ldi(a.n_sel + row);
+            n = n < 0 ? 0 : (n > kcap ? kcap : n);
+            if (r < n) {
+                int id = Mem::ldi(a.block_idx + row * a.k_max + r);
+                id = id < 0 ? 0 : (id >= nc ? nc - 1 : id);
+                atomicOr(&bm[h * W + id / 32], 1u << (id % 32));
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int base = 0;
+            for (int w0 = 0; w0 < W; w0 += 64) {
+                const int w = w0 + lane;
+                uint32_t bits[G], uni = 0u;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    bits[h] = w < W ? bm[h * W + w] : 0u;
+                    uni |= bits[h];
+                }
+                const int cnt = __popc(uni);
+                const int incl = wave_inclusive_scan(cnt, lane);
+                int pos = base + incl - cnt;
+                while (uni) {
+                    const int bit = __builtin_ctz(uni);
+                    uni &= uni - 1u;
+                    uint32_t m = 0u;
+#pragma unroll
+                    for (int h = 0; h < G; ++h) m |= ((bits[h] >> bit) & 1u) << h;
+                    uid[pos] = (uint32_t)(w * 32 + bit);
+                    umask[pos] = m;
+                    ++pos;
+                }
+                base += __builtin_amdgcn_readlane(incl, 63);
+            }
+            if (lane == 0) sm.n_union = base;
+        }
+        __syncthreads();
+        nsel = __builtin_amdgcn_readfirstlane(sm.n_union);
+    } else {
+        nsel = GT ? kcap : Mem::ldi(a.n_sel + b * a.Hkv + g);
+        nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
+    }
     const int units = nsel + (tail > 0 ? 1 : 0);
     const int u0 = (int)(((int64_t)split * units) / a.num_splits);
     const int u1 = (int)(((int64_t)(split + 1) * units) / a.num_splits);
@@ -150,7 +220,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     const uint32_t region = (uint32_t)((int64_t)a.kv_capacity * a.skv_t * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, kBufferFlags);
-    const int32_t *sel = GT ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
+    const int32_t *sel = (GT || PH) ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
     const int wt0 = wave * C::TPW;  // first token of this wave inside a unit
     uint32_t koff[C::TPL][C::CPL], voff[C::TPLV];
 #pragma unroll
@@ -164,9 +234,13 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     int ids = 0, id0 = u0 - 64;  // kept block ids of units [id0, id0 + 64), one per lane
     for (int u = u0; u < u1; ++u) {
         int tok0, cnt;
+        uint32_t hmask = (1u << G) - 1u;  // heads that take this unit
         if (u < nsel) {
             int blk = u;
-            if constexpr (!GT) {
+            if constexpr (PH) {
+                blk = (int)uid[u];
+                hmask = __builtin_amdgcn_readfirstlane(umask[u]);
+            } else if constexpr (!GT) {
                 if (u - id0 >= 64) {
                     id0 = u;
                     ids = u + lane < nsel ? Mem::ldi(sel + u + lane) : 0;
@@ -214,6 +288,14 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
             for (int t = 0; t < C::TPL; ++t)
 #pragma unroll
                 for (int h = 0; h < G; ++h) s[t][h] = wt0 + r + t * C::ROWS < cnt ? s[t][h] : -INFINITY;
+        }
+        if constexpr (PH) {  // heads that did not keep this block give it no weight
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+                if (!((hmask >> h) & 1u)) {
+#pragma unroll
+                    for (int t = 0; t < C::TPL; ++t) s[t][h] = -INFINITY;
+                }
         }
 
         // Wave-uniform running max per head (log2 domain), rescale factors, probabilities.

@@ -50,13 +50,14 @@ struct KRow<uint16_t> {
     }
 };
 
-template <int D, int NT, int G = 1, class KT = float>
+template <int D, int NT, int G = 1, class KT = float, int ITER_OVERRIDE = 0>
 struct GsCfg {
     static constexpr int NW = NT / 64;        // waves
     static constexpr int LPR = D * KRow<KT>::KB / 16;  // lanes per pooled-key row (16 bytes each)
     static constexpr int ROWS = NT / LPR;     // rows per workgroup-wide load
     // row loads in flight per thread (fewer where 1024 threads' registers also hold 8 query rows)
-    static constexpr int ITER = NT >= 1024 && D == 128 && G >= 8 && KRow<KT>::KB == 4 ? 12 : 16;
+    static constexpr int ITER =
+        ITER_OVERRIDE ? ITER_OVERRIDE : (NT >= 1024 && D == 128 && G >= 8 && KRow<KT>::KB == 4 ? 12 : 16);
     static constexpr int RPB = ROWS * ITER;   // rows per batch
     static constexpr int CH = D / 8;          // 16-byte bf16 chunks per weight row
     static constexpr int RG = NT / CH;        // weight-row groups

@@ -51,6 +51,11 @@ SIGNATURES = {
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
+    "seer_gate_select_heads": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
+                                    _P]),
+    "seer_sparse_decode_heads_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "seer_sparse_decode_heads": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I,
+                                      _I, _I, _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
     "seer_decode_block_mass_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_decode_block_mass": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _I, _I, _I, _I, _I, _F, _I,
                                     _I, _P, _SZ, _P, _I, _P, _P, _P]),
@@ -262,6 +267,44 @@ def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, soft
         k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
         block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
         _ptr(lse), _stream(stream), bind=bind)
+
+
+def seer_gate_select_heads(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, budget_tokens: int,
+                           scores, block_idx, n_sel, stream=None, bind: bool = False):
+    """Per-query-head gate scores [B, Hq, nb_max] and selections [B, Hq, budget // bs]."""
+    _bits(q), _bits(wq), _bits(wk)
+    B, Hq, d = q.shape
+    Hkv, dg, _ = wq.shape
+    assert wq.is_contiguous() and wk.is_contiguous() and kpool.is_contiguous() and scores.is_contiguous()
+    assert n_sel.is_contiguous() and scores.shape == (B, Hq, kpool.shape[2])
+    return _call(
+        "seer_gate_select_heads", _ptr(q), q.stride(0), q.stride(1), _ptr(wq), _ptr(wk), dg, _ptr(kpool),
+        kpool.shape[2], _ptr(seqlens), B, Hq, Hkv, d, block_size, float(gate_scale), budget_tokens, _ptr(scores),
+        _ptr(block_idx) if block_idx is not None and block_idx.numel() else None, _ptr(n_sel), _stream(stream),
+        bind=bind)
+
+
+def seer_sparse_decode_heads_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: int, nb_max: int,
+                                            block_size: int, num_splits: int = 0) -> int:
+    return load().seer_sparse_decode_heads_workspace_size(B, Hq, Hkv, d, k_max, nb_max, block_size, num_splits)
+
+
+def seer_sparse_decode_heads(q, k, v, seqlens, block_idx, n_sel, nb_max: int, block_size: int,
+                             softmax_scale: float, out, lse=None, workspace=None, num_splits: int = 0, stream=None,
+                             bind: bool = False):
+    """Sparse decode over per-query-head block sets (block_idx [B, Hq, k_max]): the union read once per group."""
+    _bits(q), _bits(k), _bits(v)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    assert k.stride() == v.stride() and out.is_contiguous() and block_idx.is_contiguous()
+    k_max = block_idx.shape[2]
+    out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _call(
+        "seer_sparse_decode_heads", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, int(nb_max), B,
+        Hq, Hkv, d, block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out),
+        out_dtype, _ptr(lse), _stream(stream), bind=bind)
 
 
 def seer_decode_block_mass_workspace_size(B: int, Hq: int, Hkv: int, d: int, nb_max: int, block_size: int,

@@ -209,6 +209,37 @@ int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                        void *out, int out_dtype, float *lse, hipStream_t stream);
 
 /*
+ * Per-query-head selection (the alternative GQA reading): every query head h
+ * keeps its own k = min(budget / bs, nc_b) blocks by its own gate score
+ * s_hj = gate_scale * (Wq[g] q_h) . (Wk[g] kp_j) (no group mean) and attends
+ * only those blocks plus the tail.
+ *   seer_gate_select_heads: scores fp32 [B][Hq][nb_max] (-inf past nc_b),
+ *     block_idx int32 [B][Hq][budget / bs] ascending, -1 padded, n_sel [B][Hq];
+ *     other arguments as seer_gate_select.  Hq / Hkv in {1, 2, 4, 8},
+ *     (Hq / Hkv) * nb_max <= 10240.
+ *   seer_sparse_decode_heads: out / lse as seer_sparse_decode for these per-head
+ *     sets; each block of the union of a group's sets is read once for all of
+ *     the group's heads, a head giving no weight to blocks it did not keep.
+ *     block_idx / n_sel as written above (k_max = row width), nb_max the
+ *     pooled-table width (<= 4096, bounds the block ids); workspace >=
+ *     seer_sparse_decode_heads_workspace_size(...) bytes of split partials.
+ */
+int seer_gate_select_heads(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                           const seer_bf16 *wq, const seer_bf16 *wk, int dg,
+                           const float *kpool, int nb_max, const int32_t *seqlens,
+                           int B, int Hq, int Hkv, int d, int block_size, float gate_scale, int budget_tokens,
+                           float *scores, int32_t *block_idx, int32_t *n_sel, hipStream_t stream);
+size_t seer_sparse_decode_heads_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int nb_max,
+                                               int block_size, int num_splits);
+int seer_sparse_decode_heads(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                             const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                             int kv_capacity, const int32_t *seqlens, const int32_t *block_idx,
+                             const int32_t *n_sel, int k_max, int nb_max,
+                             int B, int Hq, int Hkv, int d, int block_size, float softmax_scale, int num_splits,
+                             void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                             hipStream_t stream);
+
+/*
  * Block-level ground truth of decoding attention ("SeerAttention: Learning
  * Intrinsic Sparse Attention in Your LLMs", abstract v2: the block-level
  * ground truth of the attention map, extracted next to the attention itself;
