@@ -59,6 +59,7 @@ def _bind(path: str):
                                P, P, I, D, P, I, D, P, P, P, P, P]),
         "so_decode_step_per_head": (I, [P, I64, I64, P, P, I64, I64, I64, P, I, I, I, I, I, I,
                                         P, P, I, D, P, I, D, P, P, P, P, P]),
+        "so_prefill_block_mass": (I, [P, P, I64, I, I, I, D, I, I, P]),
         "so_prefill_gate": (I, [P, P, I64, I, I, I, P, P, I, D, I, I, P, P, P, I]),
         "so_prefill_attention": (I, [P, P, P, I64, I, I, I, P, P, I, D, I, I, P, P]),
         "so_prefill": (I, [P, P, P, I, I, I, I, I, P, P, I, D, I, I, P, P, I, D, I, I, P, P]),
@@ -274,6 +275,18 @@ def prefill_attention(q, k, v, bs: int, blocks, counts, scale: float, t_lo: int 
                                         blocks.shape[1], float(scale), t_lo, t_hi, _p(out), _p(lse)),
            "prefill_attention")
     return out, lse
+
+
+def prefill_block_mass(q, k, bs: int, scale: float, i_lo: int = 0, i_hi: Optional[int] = None) -> np.ndarray:
+    """Ground truth of one head's prefill: [i_hi - i_lo, nb] mean attention mass per (query block, key block)."""
+    q, k = _u16(q), _u16(k)
+    L, d = q.shape
+    nb = (L + bs - 1) // bs
+    i_hi = nb if i_hi is None else i_hi
+    mass = np.zeros((i_hi - i_lo, nb), dtype=np.float64)
+    _check(_load().so_prefill_block_mass(_p(q), _p(k), d, L, d, bs, float(scale), i_lo, i_hi, _p(mass)),
+           "prefill_block_mass")
+    return mass
 
 
 def prefill(q, k, v, bs: int, wq, wk, gate_scale: float, keep_num: int, keep_den: int,

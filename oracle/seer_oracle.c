@@ -623,3 +623,42 @@ int so_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, i
     }
     return bad ? -1 : 0;
 }
+
+/* ---------------------------------------------------------------- G2 --- */
+int so_prefill_block_mass(const uint16_t *q, const uint16_t *k, int64_t row_stride, int L, int d, int bs,
+                          double scale, int i_lo, int i_hi, double *mass)
+{
+    const int nb = L > 0 && bs > 0 ? (L + bs - 1) / bs : 0;
+    if (!q || !k || !mass || L <= 0 || d <= 0 || bs <= 0 || row_stride < d || i_lo < 0 || i_hi > nb ||
+        i_lo > i_hi)
+        return -1;
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    if (!z)
+        return -2;
+    for (int i = i_lo; i < i_hi; ++i) {
+        double *row = mass + (int64_t)(i - i_lo) * nb;
+        for (int j = 0; j < nb; ++j)
+            row[j] = 0.0;
+        const int t0 = i * bs, t1 = (i + 1) * bs < L ? (i + 1) * bs : L;
+        for (int t = t0; t < t1; ++t) {
+            /* dense causal softmax of row t over tokens 0..t */
+            double m = -INFINITY;
+            for (int tt = 0; tt <= t; ++tt) {
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c)
+                    dot += so_bf16_to_f64(q[(int64_t)t * row_stride + c]) *
+                           so_bf16_to_f64(k[(int64_t)tt * row_stride + c]);
+                z[tt] = scale * dot;
+                if (z[tt] > m)
+                    m = z[tt];
+            }
+            double denom = 0.0;
+            for (int tt = 0; tt <= t; ++tt)
+                denom += exp(z[tt] - m);
+            for (int tt = 0; tt <= t; ++tt)
+                row[tt / bs] += exp(z[tt] - m) / denom / (t1 - t0);
+        }
+    }
+    free(z);
+    return 0;
+}

@@ -28,6 +28,7 @@
  *     P3  row i keeps itself plus the k_i - 1 best earlier blocks,
  *         k_i = ceil((i + 1) * keep_num / keep_den)
  *     P4  causal softmax attention restricted to the kept blocks
+ *     G2  ground truth: mean attention mass of every key block per query block
  *
  * All floating point is double.  Inputs arrive as raw bf16 bit patterns
  * (uint16) and are widened exactly.  Strides are in elements.  Every
@@ -140,6 +141,14 @@ int so_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, i
                int bs, const uint16_t *wq, const uint16_t *wk, int dg, double gate_scale,
                int keep_num, int keep_den, int32_t *kv_blocks, int32_t *kv_count, int kmax_row,
                double scale, int t_lo, int t_hi, double *out, double *lse);
+
+/* G2, the block-level ground truth of prefill attention (same source as G1):
+ * dense causal softmax attention of one head, and for query blocks i in
+ * [i_lo, i_hi) and key blocks j <= i the mean over block i's rows t of the
+ * weight row t gives to the tokens of block j (t' <= t).  nb = ceil(L / bs);
+ * mass [(i_hi - i_lo)][nb], zero for j > i; each row block sums to 1. */
+int so_prefill_block_mass(const uint16_t *q, const uint16_t *k, int64_t row_stride, int L, int d, int bs,
+                          double scale, int i_lo, int i_hi, double *mass);
 
 #ifdef __cplusplus
 }

@@ -83,3 +83,54 @@ def test_group_mass_is_the_mean_of_the_heads():
     _, _, m = oracle.decode_block_mass(q, k, v, 64, 0.125)
     per = [oracle.decode_block_mass(q[h:h + 1], k, v, 64, 0.125)[2] for h in range(3)]
     np.testing.assert_allclose(m, np.mean(per, axis=0), rtol=0, atol=1e-14)
+
+
+# ---- prefill (G2): per (query block, key block) mean attention mass under dense causal attention ----
+
+def torch_prefill_mass(q, k, bs, scale):
+    qd, kd = widen(q), widen(k)
+    L = qd.shape[0]
+    logits = (qd @ kd.T) * scale
+    causal = torch.ones(L, L, dtype=torch.bool).tril()
+    w = torch.softmax(logits.masked_fill(~causal, -math.inf), dim=-1)    # [L, L]
+    nb = (L + bs - 1) // bs
+    out = torch.zeros(nb, nb, dtype=torch.float64)
+    for i in range(nb):
+        rows = w[i * bs:(i + 1) * bs]
+        for j in range(i + 1):
+            out[i, j] = rows[:, j * bs:(j + 1) * bs].sum(-1).mean()
+    return out.numpy()
+
+
+@pytest.mark.parametrize("L,bs", [(256, 64), (300, 64), (64, 64), (5, 64), (1000, 128)])
+def test_prefill_mass_equals_torch_causal_softmax(L, bs):
+    q, k, _ = rand_case(1, 64, L, seed=L + 1)
+    q = rand_case(L, 64, 1, seed=L + 2)[0]          # L query rows
+    mass = oracle.prefill_block_mass(q, k, bs, 0.125)
+    np.testing.assert_allclose(mass, torch_prefill_mass(q, k, bs, 0.125), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mass.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(np.triu(mass, 1) == 0.0)
+
+
+def test_prefill_mass_equal_keys_closed_form():
+    """Equal keys: row t spreads 1/(t+1) over tokens 0..t."""
+    L, bs = 200, 64
+    g = torch.Generator().manual_seed(9)
+    q = bf16(torch.randn(L, 32, generator=g))
+    k = bf16(torch.randn(1, 32, generator=g).expand(L, 32).contiguous())
+    mass = oracle.prefill_block_mass(q, k, bs, 0.2)
+    nb = (L + bs - 1) // bs
+    expect = np.zeros((nb, nb))
+    for i in range(nb):
+        ts = range(i * bs, min((i + 1) * bs, L))
+        for j in range(i + 1):
+            expect[i, j] = np.mean([max(0, min(t + 1, (j + 1) * bs) - j * bs) / (t + 1) for t in ts])
+    np.testing.assert_allclose(mass, expect, rtol=0, atol=1e-12)
+
+
+def test_prefill_mass_row_range_matches_full():
+    q = rand_case(500, 64, 1, seed=3)[0]
+    k = rand_case(1, 64, 500, seed=4)[1]
+    full = oracle.prefill_block_mass(q, k, 64, 0.125)
+    part = oracle.prefill_block_mass(q, k, 64, 0.125, 3, 6)
+    np.testing.assert_allclose(part, full[3:6], rtol=0, atol=0)

@@ -77,6 +77,9 @@ MUTATIONS = [
      "if (exp(S[j] - m) >= tau)", lambda: T_pol.test_threshold_keeps_the_blocks_above_tau(64, 0.02)),
     ("per-head variant selects from the group mean", "int n = so_select_blocks(sh + (int64_t)h * nc, nc, kmax, sel);",
      "int n = so_select_blocks(S, nc, kmax, sel);", T_ph.test_heads_differ_and_each_head_is_its_own_masked_attention),
+    ("prefill ground truth averaged over the block size, not its rows",
+     "row[tt / bs] += exp(z[tt] - m) / denom / (t1 - t0);", "row[tt / bs] += exp(z[tt] - m) / denom / bs;",
+     lambda: T_gt.test_prefill_mass_equals_torch_causal_softmax(300, 64)),
     ("prefill causal mask dropped", "for (int tt = 0; tt <= t; ++tt)", "for (int tt = 0; tt < L; ++tt)",
      lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
 ]
