@@ -490,11 +490,28 @@ def bench_prefill(steps, dev):
 
     us_total = timed(False)
     us_attn = timed(True)
+    # ground truth: dense causal attention plus every (query block, key block) mass
+    mass = torch.empty((pw.B, pw.H, nb, nb), dtype=torch.float32, device=dev)
+    gt = seer.seer_prefill_block_mass(x["q"], x["k"], x["v"], pw.bs, ss, out, mass, lse, bind=True)
+    gt()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gt()
+    e1.record()
+    torch.cuda.synchronize()
+    us_gt = e0.elapsed_time(e1) * 1e3
+    causal_blocks = nb * (nb + 1) // 2
+    dense_flops = (causal_blocks - nb) * 4 * pw.bs * pw.bs * pw.d + nb * 4 * (pw.bs * (pw.bs + 1) // 2) * pw.d
+    del mass
     flops = prefill_flops(counts, pw.bs, pw.d)
     tflops = flops / (us_attn * 1e-6) / 1e12
     return {"workload": pw.name, "steps": steps, "us_per_prefill": round(us_total, 1),
             "us_gate": round(us_total - us_attn, 1), "us_attention": round(us_attn, 1),
             "kept_blocks_per_head": int(counts[0, 0].sum()), "algorithmic_gflop": round(flops / 1e9, 1),
+            "ground_truth": {"call": "seer_prefill_block_mass", "us": round(us_gt, 1),
+                             "dense_attention_gflop": round(pw.B * pw.H * dense_flops / 1e9, 1),
+                             "note": "dense causal attention + a second QK sweep for every block's mean mass"},
             "roofline": {"kernel": "prefill_attention_kernel", "bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}

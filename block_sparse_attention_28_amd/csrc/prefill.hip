@@ -211,12 +211,17 @@ __device__ __forceinline__ int vt_index(int d, int key) {  // V^T[d][key], 4-key
     return d * kPBS + ((((key >> 2) ^ swz) & 15) << 2) + (key & 3);
 }
 
-template <int D>
+// GT (the ground-truth form): every causal block j <= i is attended (the lists
+// are not read), and after the output a second sweep over K recomputes the
+// scores and writes mass[b][h][i][j] = mean over block i's rows of the weight
+// they give block j (zero for j > i).
+template <int D, bool GT = false>
 __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_t *q, const uint16_t *k,
                                                                    const uint16_t *v, int H, int L, int nb,
                                                                    const int32_t *kv_blocks,
                                                                    const int32_t *kv_count, int kmax_row,
-                                                                   float scale_log2, uint16_t *out, float *lse) {
+                                                                   float scale_log2, uint16_t *out, float *lse,
+                                                                   float *mass) {
     constexpr int KS = D / 32;           // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;           // 16-wide d tiles of O^T
     constexpr int KPAD = D + 8;          // K row stride in LDS (elements)
@@ -252,13 +257,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     float m_run = -INFINITY, l_run = 0.f;
 
     const int64_t row = ((int64_t)b * H + h) * nb + i;
-    int cnt = kv_count[row];
+    int cnt = GT ? i + 1 : kv_count[row];
     cnt = cnt < 0 ? 0 : (cnt > kmax_row ? kmax_row : cnt);
-    const int32_t *blist = kv_blocks + row * kmax_row;
+    const int32_t *blist = GT ? nullptr : kv_blocks + row * kmax_row;
+    auto block_of = [&](int it) { return GT ? it : blist[it]; };
 
     uint4 kreg[KCH], vreg[VPR][2];
     auto fetch = [&](int it) {
-        int j = blist[it];
+        int j = block_of(it);
         j = j < 0 ? 0 : (j > i ? i : j);
         const int k0 = j * kPBS;
 #pragma unroll
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     if (cnt > 0) fetch(0);
 
     for (int it = 0; it < cnt; ++it) {
-        int j = blist[it];
+        int j = block_of(it);
         j = j < 0 ? 0 : (j > i ? i : j);
         const int k0 = j * kPBS;
         __syncthreads();  // previous block's LDS reads are done
@@ -378,6 +384,47 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         }
         if (g == 0 && lse) lse[((int64_t)b * H + h) * L + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }
+    if constexpr (GT) {
+        // Second sweep: each block's share of every row's softmax, averaged over the block's rows.
+        __shared__ float red[4];
+        const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : INFINITY;
+        const int rows_i = L - i * kPBS < kPBS ? L - i * kPBS : kPBS;
+        float *mrow = mass + row * nb;
+        for (int j = i + 1 + tid; j < nb; j += 256) mrow[j] = 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const int k0 = j * kPBS;
+            __syncthreads();  // previous readers of k_lds and red are done
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
+                const int tok = k0 + r;
+                const uint4 w = tok < L ? *reinterpret_cast<const uint4 *>(kh + (int64_t)tok * D + cc * 8)
+                                        : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(&k_lds[r * KPAD + cc * 8]) = w;
+            }
+            __syncthreads();
+            float psum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&k_lds[(16 * t + n) * KPAD + 8 * g + 32 * ks]);
+                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], st, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ktok = k0 + 16 * t + 4 * g + e;
+                    const bool live = ktok <= qtok && ktok < L && qtok < L;
+                    psum += live ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
+                }
+            }
+            psum = wave_sum(psum);
+            if (lane == 0) red[wave] = psum;
+            __syncthreads();
+            if (tid == 0) mrow[j] = (red[0] + red[1] + red[2] + red[3]) / (float)rows_i;
+        }
+    }
 }
 
 }  // namespace seer
@@ -441,6 +488,21 @@ extern "C" int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k,
         if ((st = launch_status()) != SEER_OK) return st;
     }
     prefill_attention_kernel<128><<<dim3((unsigned)rows), 256, 0, stream>>>(
-        q, k, v, H, L, nb, kv_blocks, kv_count, kmax_row, softmax_scale * kLog2e, out, lse);
+        q, k, v, H, L, nb, kv_blocks, kv_count, kmax_row, softmax_scale * kLog2e, out, lse, nullptr);
+    return launch_status();
+}
+
+extern "C" int seer_prefill_block_mass(const seer_bf16 *q, const seer_bf16 *k, const seer_bf16 *v, int B, int H,
+                                       int L, int d, int block_size, float softmax_scale, seer_bf16 *out, float *lse,
+                                       float *mass, hipStream_t stream) {
+    if (!q || !k || !v || !out || !mass) return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || L <= 0 || !(softmax_scale == softmax_scale)) return SEER_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SEER_ERR_INVALID_ARG;
+    if (d != 128 || block_size != kPBS) return SEER_ERR_UNSUPPORTED;
+    const int nb = (L + kPBS - 1) / kPBS;
+    const int64_t rows = (int64_t)B * H * nb;
+    if (rows > 0x7fffffffLL) return SEER_ERR_INVALID_ARG;
+    prefill_attention_kernel<128, true><<<dim3((unsigned)rows), 256, 0, stream>>>(
+        q, k, v, H, L, nb, nullptr, nullptr, nb, softmax_scale * kLog2e, out, lse, mass);
     return launch_status();
 }

@@ -59,6 +59,7 @@ SIGNATURES = {
     "seer_decode_block_mass_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_decode_block_mass": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _I, _I, _I, _I, _I, _F, _I,
                                     _I, _P, _SZ, _P, _I, _P, _P, _P]),
+    "seer_prefill_block_mass": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P]),
     "seer_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_decode_step": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _F, _P, _I, _I, _I, _I,
                               _I, _I, _I, _F, _I, _P, _P, _P, _P, _SZ, _P, _I, _P, _P]),
@@ -352,6 +353,19 @@ def seer_block_sparse_prefill(q, k, v, block_size: int, wq, wk, gate_scale: floa
           float(gate_scale), keep_num, keep_den, _ptr(kv_blocks), _ptr(kv_count), kv_blocks.shape[-1],
           1 if use_given_blocks else 0, float(softmax_scale), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
           _stream(stream))
+
+
+def seer_prefill_block_mass(q, k, v, block_size: int, softmax_scale: float, out, mass, lse=None, stream=None,
+                            bind: bool = False):
+    """Dense causal attention of q, k, v [B, H, L, d] into out, and mass [B, H, nb, nb]: per query block the
+    mean attention mass of every key block."""
+    _bits(q), _bits(k), _bits(v), _bits(out)
+    B, H, L, d = q.shape
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous() and out.is_contiguous()
+    assert mass.dtype == torch.float32 and mass.is_contiguous()
+    return _call(
+        "seer_prefill_block_mass", _ptr(q), _ptr(k), _ptr(v), B, H, L, d, block_size, float(softmax_scale),
+        _ptr(out), _ptr(lse), _ptr(mass), _stream(stream), bind=bind)
 
 
 def seer_decode_step_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: int, block_size: int,

@@ -341,6 +341,22 @@ int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k, const seer
                               void *workspace, size_t workspace_bytes, seer_bf16 *out, float *lse,
                               hipStream_t stream);
 
+/*
+ * Block-level ground truth of prefill attention ("SeerAttention: Learning
+ * Intrinsic Sparse Attention in Your LLMs", abstract v2: the block-level
+ * ground truth of the attention map, extracted next to the attention with a
+ * customised FlashAttention).  Dense causal attention (out, lse as
+ * seer_block_sparse_prefill with every causal block kept), then for query
+ * block i and key block j <= i
+ *   mass[b][h][i][j] = mean over the rows t of block i of sum_{t' in block j, t' <= t} softmax_t(t')
+ * and 0 for j > i; each row block sums to 1.
+ *   mass  fp32 [B][H][nb][nb], nb = ceil(L / block_size); lse may be NULL
+ * d = 128, block_size = 64.
+ */
+int seer_prefill_block_mass(const seer_bf16 *q, const seer_bf16 *k, const seer_bf16 *v, int B, int H, int L,
+                            int d, int block_size, float softmax_scale, seer_bf16 *out, float *lse, float *mass,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

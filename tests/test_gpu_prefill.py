@@ -148,3 +148,56 @@ def test_prefill_full_size_sampled():
     for h in heads:
         say(f"  oracle head {h}")
         check_head(w, x, blocks, counts, out, lse, 0, h, ranges)
+
+
+# ---- block-level ground truth of prefill attention ----
+
+def run_mass(w: PrefillWorkload):
+    say(f"[gpu] prefill block mass {w.name} L={w.L}")
+    x = inputs.prefill_inputs(w, "cuda")
+    nb = (w.L + w.bs - 1) // w.bs
+    mass = torch.full((w.B, w.H, nb, nb), float("nan"), device="cuda")
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device="cuda")
+    seer.seer_prefill_block_mass(x["q"], x["k"], x["v"], w.bs, 1 / math.sqrt(w.d), out, mass, lse)
+    torch.cuda.synchronize()
+    return x, mass, out, lse, nb
+
+
+MASS_CASES = [SMALL[0], SMALL[2], SMALL[4], SMALL[5],
+              PrefillWorkload(name="p300_mass", B=2, H=2, L=300, d=128, bs=64, keep_num=1, keep_den=1, seed=49)]
+
+
+@pytest.mark.parametrize("w", MASS_CASES, ids=[w.name for w in MASS_CASES])
+def test_prefill_block_mass_small_full(w):
+    x, mass, out, lse, nb = run_mass(w)
+    gm = mass.cpu().double().numpy()
+    assert np.abs(gm.sum(-1) - 1.0).max() <= 1e-4
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = oracle.prefill_block_mass(host_bits(x["q"][b, h]), host_bits(x["k"][b, h]), w.bs, 1 / math.sqrt(w.d))
+            np.testing.assert_allclose(gm[b, h], ref, rtol=0, atol=2e-5)
+    # the dense output is bit-identical to the block-sparse prefill given every causal block
+    blocks = torch.full((w.B, w.H, nb, nb), -1, dtype=torch.int32)
+    for i in range(nb):
+        blocks[:, :, i, :i + 1] = torch.arange(i + 1, dtype=torch.int32)
+    counts = (torch.arange(nb, dtype=torch.int32) + 1).expand(w.B, w.H, nb).contiguous()
+    out2 = torch.full_like(out, float("nan"))
+    lse2 = torch.empty_like(lse)
+    seer.seer_block_sparse_prefill(x["q"], x["k"], x["v"], w.bs, None, None, 1.0, 1, 1, blocks.cuda(), counts.cuda(),
+                                   1 / math.sqrt(w.d), out2, lse2, None, use_given_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_prefill_block_mass_32k_sampled_rows():
+    w = PREFILL_L32K
+    x, mass, out, lse, nb = run_mass(w)
+    assert torch.all((mass.sum(-1) - 1.0).abs() <= 1e-4)
+    assert torch.all(mass.triu(1) == 0)
+    for h in (0, w.H - 1):
+        for i0 in (0, nb // 2, nb - 2):
+            say(f"  oracle head {h} row blocks {i0}..{i0 + 1}")
+            ref = oracle.prefill_block_mass(host_bits(x["q"][0, h]), host_bits(x["k"][0, h]), w.bs,
+                                            1 / math.sqrt(w.d), i0, i0 + 2)
+            np.testing.assert_allclose(mass[0, h, i0:i0 + 2].cpu().double().numpy(), ref, rtol=0, atol=2e-5)
