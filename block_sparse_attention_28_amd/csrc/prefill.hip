@@ -206,9 +206,16 @@ __global__ __launch_bounds__(256) void prefill_select_rows_kernel(const float *S
 }
 
 // ----------------------------------------------------------- attention ----
-__device__ __forceinline__ int vt_index(int d, int key) {  // V^T[d][key], 4-key groups XOR-swizzled by row
-    const int swz = (d ^ (d >> 3)) & 15;
-    return d * kPBS + ((((key >> 2) ^ swz) & 15) << 2) + (key & 3);
+// V^T in LDS: row d holds the block's 64 keys as 8 groups of 8 keys (16 bytes),
+// group (ks, g) = keys 32ks + 4g + 0..3 followed by 32ks + 16 + 4g + 0..3, the
+// order in which lane (g, n) supplies k-slots 8g..8g+7 of P^T for k-step ks,
+// so one 16-byte read gives a lane its V^T operand.  Groups are XOR-swizzled by
+// the row against bank conflicts.  Byte offset of (d, key):
+__device__ __forceinline__ int vt_byte(int d, int key) {
+    const int ks = key >> 5, kk = key & 31;
+    const int sg = 4 * ks + ((kk & 15) >> 2);
+    const int slot = (kk & 3) + ((kk >> 4) << 2);
+    return d * (kPBS * 2) + ((sg ^ ((d ^ (d >> 3)) & 7)) << 4) + slot * 2;
 }
 
 // GT (the ground-truth form): every causal block j <= i is attended (the lists
@@ -262,24 +269,65 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     const int32_t *blist = GT ? nullptr : kv_blocks + row * kmax_row;
     auto block_of = [&](int it) { return GT ? it : blist[it]; };
 
+    // K and V of the head through buffer descriptors: a block's first row is a
+    // scalar byte offset, each thread's chunks fixed 32-bit offsets.  In the
+    // last block of a context that is not a multiple of 64, rows past the end
+    // read the last token instead (their scores are masked, their weights 0).
+    const uint32_t head_bytes = (uint32_t)((int64_t)L * D * 2);
+    const auto krs = buffer_rsrc(kh, head_bytes), vrs = buffer_rsrc(vh, head_bytes);
+    uint32_t koff[KCH], voff[VPR];
+    int krow[KCH], vrow[VPR];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const int ch = tid + 256 * c;
+        krow[c] = ch / CPR;
+        koff[c] = (uint32_t)((ch / CPR) * D * 2 + (ch % CPR) * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < VPR; ++c) {
+        const int item = tid + 256 * c;
+        vrow[c] = 2 * (item / CPR);
+        voff[c] = (uint32_t)(vrow[c] * D * 2 + (item % CPR) * 16);
+    }
+    // LDS byte offsets of this thread's V^T stores (two keys per 32-bit word).
+    uint32_t vst[VPR][8];
+#pragma unroll
+    for (int c = 0; c < VPR; ++c) {
+        const int item = tid + 256 * c, cc = item % CPR;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            vst[c][2 * e2] = (uint32_t)vt_byte(cc * 8 + 2 * e2, vrow[c]);
+            vst[c][2 * e2 + 1] = (uint32_t)vt_byte(cc * 8 + 2 * e2 + 1, vrow[c]);
+        }
+    }
+    char *vt_bytes = reinterpret_cast<char *>(vt_lds);
+
     uint4 kreg[KCH], vreg[VPR][2];
     auto fetch = [&](int it) {
         int j = block_of(it);
         j = j < 0 ? 0 : (j > i ? i : j);
         const int k0 = j * kPBS;
+        if (k0 + kPBS <= L) {  // a whole block: scalar row offset
+            const uint32_t soff = (uint32_t)k0 * D * 2;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
-            const int tok = k0 + r;
-            kreg[c] = tok < L ? *reinterpret_cast<const uint4 *>(kh + (int64_t)tok * D + cc * 8) : make_uint4(0, 0, 0, 0);
-        }
+            for (int c = 0; c < KCH; ++c) kreg[c] = buf_ld16(krs, koff[c], soff);
 #pragma unroll
-        for (int c = 0; c < VPR; ++c) {
-            const int item = tid + 256 * c, rp = item / CPR, cc = item % CPR;
-            const int tok = k0 + 2 * rp;
-            vreg[c][0] = tok < L ? *reinterpret_cast<const uint4 *>(vh + (int64_t)tok * D + cc * 8) : make_uint4(0, 0, 0, 0);
-            vreg[c][1] = tok + 1 < L ? *reinterpret_cast<const uint4 *>(vh + (int64_t)(tok + 1) * D + cc * 8)
-                                     : make_uint4(0, 0, 0, 0);
+            for (int c = 0; c < VPR; ++c) {
+                vreg[c][0] = buf_ld16(vrs, voff[c], soff);
+                vreg[c][1] = buf_ld16(vrs, voff[c] + D * 2, soff);
+            }
+        } else {  // the context's partial last block
+            auto clamped = [&](int r, uint32_t off) {
+                const int tok = k0 + r < L ? k0 + r : L - 1;
+                return (uint32_t)((tok - r) * D * 2) + off;
+            };
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) kreg[c] = buf_ld16(krs, clamped(krow[c], koff[c]), 0);
+#pragma unroll
+            for (int c = 0; c < VPR; ++c) {
+                vreg[c][0] = buf_ld16(vrs, clamped(vrow[c], voff[c]), 0);
+                vreg[c][1] = buf_ld16(vrs, clamped(vrow[c] + 1, voff[c] + D * 2), 0);
+            }
         }
     };
     if (cnt > 0) fetch(0);
@@ -296,15 +344,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         }
 #pragma unroll
         for (int c = 0; c < VPR; ++c) {
-            const int item = tid + 256 * c, rp = item / CPR, cc = item % CPR;
             const uint32_t a4[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
             const uint32_t b4[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                const uint32_t lo = (a4[e2] & 0xffffu) | (b4[e2] << 16);           // column 2*e2
-                const uint32_t hi = (a4[e2] >> 16) | (b4[e2] & 0xffff0000u);       // column 2*e2+1
-                *reinterpret_cast<uint32_t *>(&vt_lds[vt_index(cc * 8 + 2 * e2, 2 * rp)]) = lo;
-                *reinterpret_cast<uint32_t *>(&vt_lds[vt_index(cc * 8 + 2 * e2 + 1, 2 * rp)]) = hi;
+                // (row 2rp, row 2rp+1) of column 2*e2, then of column 2*e2+1
+                const uint32_t lo = __builtin_amdgcn_perm(b4[e2], a4[e2], 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(b4[e2], a4[e2], 0x07060302u);
+                *reinterpret_cast<uint32_t *>(vt_bytes + vst[c][2 * e2]) = lo;
+                *reinterpret_cast<uint32_t *>(vt_bytes + vst[c][2 * e2 + 1]) = hi;
             }
         }
         __syncthreads();
@@ -321,19 +369,26 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                 s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], s[t], 0, 0, 0);
             }
         }
-        // Lane holds keys 16t + 4g + e of query row qtok; causal + length masks.
+        // Lane holds keys 16t + 4g + e of query row qtok.  Only the diagonal block
+        // and a partial last block need the causal / length masks.
         float mloc = -INFINITY;
+        if (j == i || k0 + kPBS > L) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ktok = k0 + 16 * t + 4 * g + e;
-                float x = s[t][e] * scale_log2;
-                x = (ktok > qtok || ktok >= L) ? -INFINITY : x;
-                s[t][e] = x;
-                mloc = fmax_fast(mloc, x);
-            }
-        mloc = max_xor32(max_xor16(mloc));  // the 4 lanes of this query row
+                for (int e = 0; e < 4; ++e) {
+                    const int ktok = k0 + 16 * t + 4 * g + e;
+                    const float x = (ktok > qtok || ktok >= L) ? -INFINITY : s[t][e];
+                    s[t][e] = x;
+                    mloc = fmax_fast(mloc, x);
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mloc = fmax_fast(mloc, s[t][e]);
+        }
+        mloc = max_xor32(max_xor16(mloc)) * scale_log2;  // the 4 lanes of this query row; scale > 0
         const float m_new = fmax_fast(m_run, mloc);
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_ref);
@@ -343,13 +398,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = fast_exp2(s[t][e] - m_ref);
+                const float p = fast_exp2(fmaf(s[t][e], scale_log2, -m_ref));
                 s[t][e] = p;
                 lsum += p;
             }
         l_run = l_run * alpha + lsum;
+        if (__ballot(alpha != 1.0f)) {  // some row's maximum moved
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        }
         // P^T operand: k-slots 8g..8g+3 <- keys 32ks + 4g + e, 8g+4..8g+7 <- keys 32ks + 16 + 4g + e.
         bf16x8_t pb[2];
 #pragma unroll
@@ -364,9 +421,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
             const int dcol = 16 * dt + n;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const uint2 lo = *reinterpret_cast<const uint2 *>(&vt_lds[vt_index(dcol, 32 * ks + 4 * g)]);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(&vt_lds[vt_index(dcol, 32 * ks + 16 + 4 * g)]);
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                const int sg = 4 * ks + g;
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+                    vt_bytes + dcol * (kPBS * 2) + ((sg ^ ((dcol ^ (dcol >> 3)) & 7)) << 4));
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], oacc[dt], 0, 0, 0);
             }
         }
