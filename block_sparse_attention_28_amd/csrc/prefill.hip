@@ -16,18 +16,22 @@
 //                          lower-triangular tiles only
 //   prefill_select_rows  : one wave per row: exact top-(k_i - 1) of j < i with
 //                          lower-id ties, then the diagonal
-//   prefill_attention    : 64 query rows per workgroup (16 per wave), MFMA
+//   prefill_attention    : 64 query rows per workgroup; each wave takes 32
+//                          rows and one 32-key half of every kept block, MFMA
 //                          v_mfma_f32_16x16x32_bf16.  S^T = K Q^T so that each
 //                          lane holds one query row's probabilities in exactly
 //                          the operand layout of O^T = V^T P^T; K is staged in
-//                          LDS row-major, V transposed (XOR-swizzled 4-key
-//                          groups); the next kept block's K/V are prefetched
-//                          into registers while the current one is computed.
+//                          LDS row-major, V transposed, both XOR-swizzled
+//                          against bank conflicts; the next kept block's K/V
+//                          are prefetched into registers while the current one
+//                          is computed, and the two key halves of each row are
+//                          merged once at the end.
 #include "seer_device.hpp"
 #include "seer_host.hpp"
 #include "topk_wave.hpp"
 
 #include <math.h>
+#include <type_traits>
 
 namespace seer {
 
@@ -35,6 +39,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPBS = 64;  // prefill block size (query and key blocks)
+constexpr float kLazyRescale = 8.0f;  // largest log2 weight before the running reference moves
 
 __device__ __forceinline__ int keep_count(int i, int num, int den) {
     const int64_t k = ((int64_t)(i + 1) * num + den - 1) / den;
@@ -206,16 +211,25 @@ __global__ __launch_bounds__(256) void prefill_select_rows_kernel(const float *S
 }
 
 // ----------------------------------------------------------- attention ----
-// V^T in LDS: row d holds the block's 64 keys as 8 groups of 8 keys (16 bytes),
-// group (ks, g) = keys 32ks + 4g + 0..3 followed by 32ks + 16 + 4g + 0..3, the
-// order in which lane (g, n) supplies k-slots 8g..8g+7 of P^T for k-step ks,
-// so one 16-byte read gives a lane its V^T operand.  Groups are XOR-swizzled by
-// the row against bank conflicts.  Byte offset of (d, key):
+// Workgroup of 4 waves per 64-row query block.  Wave w owns query rows
+// 32 * (w & 1) + 0..31 (two 16-row MFMA tiles) and keys 32 * (w >> 1) + 0..31 of
+// every kept key block, so each K / V element staged in LDS is read by two
+// waves instead of four; the two key halves of a row are merged once at the end
+// (their running maxima and sums combine as in split-KV decoding).
+//
+// LDS layouts (one 64-key block; bank behaviour measured on gfx950):
+//  K   : key rows of 256 bytes, 16-byte chunk c of key r stored at chunk
+//        c ^ (r & 15), so the 16 keys x 16 bytes of an MFMA A operand, and the
+//        8-lane groups of the staging writes, hit distinct banks.
+//  V^T : d rows of 128 bytes holding the 64 keys as 8 groups of 8 (16 bytes);
+//        group sg = 4 * (key >> 5) + ((key >> 2) & 3) lists keys in the order
+//        lane (g, n) supplies k-slots 8g..8g+7 of P^T (key & 3, then bit 4),
+//        and sits at position sg ^ (((d >> 1) ^ (d >> 4)) & 7) of its row.
+__device__ __forceinline__ int vt_group_pos(int d, int sg) { return (sg ^ ((d >> 1) ^ (d >> 4))) & 7; }
 __device__ __forceinline__ int vt_byte(int d, int key) {
-    const int ks = key >> 5, kk = key & 31;
-    const int sg = 4 * ks + ((kk & 15) >> 2);
-    const int slot = (kk & 3) + ((kk >> 4) << 2);
-    return d * (kPBS * 2) + ((sg ^ ((d ^ (d >> 3)) & 7)) << 4) + slot * 2;
+    const int sg = 4 * (key >> 5) + ((key >> 2) & 3);
+    const int slot = (key & 3) + (((key >> 4) & 1) << 2);
+    return d * (kPBS * 2) + (vt_group_pos(d, sg) << 4) + slot * 2;
 }
 
 // GT (the ground-truth form): every causal block j <= i is attended (the lists
@@ -229,39 +243,56 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                                                                    const int32_t *kv_count, int kmax_row,
                                                                    float scale_log2, uint16_t *out, float *lse,
                                                                    float *mass) {
+    static_assert(D == 128, "the LDS layouts assume 256-byte key rows");
     constexpr int KS = D / 32;           // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;           // 16-wide d tiles of O^T
-    constexpr int KPAD = D + 8;          // K row stride in LDS (elements)
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int KCH = kPBS * CPR / 256;        // K chunks per thread
-    constexpr int VPR = (kPBS / 2) * CPR / 256;  // V row-pair chunks per thread
-    __shared__ __align__(16) uint16_t k_lds[kPBS * KPAD];
-    __shared__ __align__(16) uint16_t vt_lds[D * kPBS];
+    constexpr int CPR = D / 8;           // 16-byte chunks per key row
+    constexpr int KCH = kPBS * CPR / 256;        // K chunks staged per thread
+    constexpr int VPR = (kPBS / 2) * CPR / 256;  // V (row pair, chunk) items per thread
+    constexpr int KBYTES = kPBS * D * 2;
+    // Two K buffers, then two V^T buffers during the sweep; the key-half
+    // exchange (2 waves x 2 tiles x DT x 256 floats) after it.
+    __shared__ __align__(16) char smem[4 * KBYTES];
+    __shared__ float xml[2][2][2][64];   // [rh][tile][m | l][lane] of the key-half-1 waves
+    static_assert(2 * 2 * DT * 256 * 4 <= 2 * KBYTES, "exchange fits the staging area");
+    char *const k_lds = smem, *const vt_lds = smem + 2 * KBYTES;  // buffer b at + b * KBYTES
 
-    // Longest rows first: within each (b, h) the last query block comes first.
-    const int64_t wi = blockIdx.x;
+    // Workgroups reach the 8 XCDs round-robin (id % 8); give each XCD one
+    // contiguous range of the (b, h)-major list so that a head's K / V blocks
+    // are fetched into one L2 instead of all eight.  Longest rows first: within
+    // each (b, h) the last query block comes first.
+    const int64_t nwg = gridDim.x, xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    const int64_t wi = xcd * (nwg / 8) + (xcd < nwg % 8 ? xcd : nwg % 8) + local;
     const int64_t per_b = (int64_t)H * nb;
     const int b = (int)(wi / per_b);
     const int rem = (int)(wi % per_b);
     const int h = rem / nb;
     const int i = nb - 1 - rem % nb;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rh = wave & 1, kh = wave >> 1;
     const int g = lane >> 4, n = lane & 15;
     const int64_t head = ((int64_t)b * H + h) * L * D;
-    const uint16_t *qh = q + head, *kh = k + head, *vh = v + head;
-    const int qtok = i * kPBS + wave * 16 + n;  // this lane's query row
+    const uint16_t *qh = q + head, *kh_ptr = k + head, *vh = v + head;
+    int qtok[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) qtok[r] = i * kPBS + 32 * rh + 16 * r + n;  // this lane's query rows
 
-    bf16x8_t qop[KS];
+    bf16x8_t qop[2][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 w = qtok < L ? *reinterpret_cast<const uint4 *>(qh + (int64_t)qtok * D + 8 * g + 32 * ks)
-                           : make_uint4(0, 0, 0, 0);
-        qop[ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
-    f32x4_t oacc[DT];
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 w = qtok[r] < L ? *reinterpret_cast<const uint4 *>(qh + (int64_t)qtok[r] * D + 8 * g + 32 * ks)
+                                  : make_uint4(0, 0, 0, 0);
+            qop[r][ks] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    f32x4_t oacc[2][DT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[r][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
     const int64_t row = ((int64_t)b * H + h) * nb + i;
     int cnt = GT ? i + 1 : kv_count[row];
@@ -274,212 +305,318 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // last block of a context that is not a multiple of 64, rows past the end
     // read the last token instead (their scores are masked, their weights 0).
     const uint32_t head_bytes = (uint32_t)((int64_t)L * D * 2);
-    const auto krs = buffer_rsrc(kh, head_bytes), vrs = buffer_rsrc(vh, head_bytes);
-    uint32_t koff[KCH], voff[VPR];
+    const auto krs = buffer_rsrc(kh_ptr, head_bytes), vrs = buffer_rsrc(vh, head_bytes);
+    uint32_t koff[KCH], kst[KCH], voff[VPR];
     int krow[KCH], vrow[VPR];
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-        const int ch = tid + 256 * c;
-        krow[c] = ch / CPR;
-        koff[c] = (uint32_t)((ch / CPR) * D * 2 + (ch % CPR) * 16);
+        const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
+        krow[c] = r;
+        koff[c] = (uint32_t)(r * D * 2 + cc * 16);
+        kst[c] = (uint32_t)(r * D * 2 + ((cc ^ (r & 15)) << 4));
     }
+    // V items: lane bits 0-2 pick the 16-byte column chunk, bit 3 row-pair bit 0,
+    // bit 4 row-pair bit 3, bit 5 chunk bit 3; the wave gives row-pair bits 1-2 and
+    // the item index bit 4.  With the V^T layout above every 32-lane half of each
+    // 4-byte store then covers the 32 banks once.
+    uint32_t vst[VPR][4];
 #pragma unroll
     for (int c = 0; c < VPR; ++c) {
-        const int item = tid + 256 * c;
-        vrow[c] = 2 * (item / CPR);
-        voff[c] = (uint32_t)(vrow[c] * D * 2 + (item % CPR) * 16);
-    }
-    // LDS byte offsets of this thread's V^T stores (two keys per 32-bit word).
-    uint32_t vst[VPR][8];
+        const int cc = (lane & 7) + 8 * (lane >> 5);
+        const int rp = ((lane >> 3) & 1) + 2 * (wave & 1) + 4 * (wave >> 1) + 8 * ((lane >> 4) & 1) + 16 * c;
+        vrow[c] = 2 * rp;
+        voff[c] = (uint32_t)(vrow[c] * D * 2 + cc * 16);
 #pragma unroll
-    for (int c = 0; c < VPR; ++c) {
-        const int item = tid + 256 * c, cc = item % CPR;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            vst[c][2 * e2] = (uint32_t)vt_byte(cc * 8 + 2 * e2, vrow[c]);
-            vst[c][2 * e2 + 1] = (uint32_t)vt_byte(cc * 8 + 2 * e2 + 1, vrow[c]);
-        }
+        for (int e2 = 0; e2 < 4; ++e2) vst[c][e2] = (uint32_t)vt_byte(cc * 8 + 2 * e2, vrow[c]);
     }
-    char *vt_bytes = reinterpret_cast<char *>(vt_lds);
 
     uint4 kreg[KCH], vreg[VPR][2];
-    auto fetch = [&](int it) {
+    auto block_start = [&](int it) {
         int j = block_of(it);
         j = j < 0 ? 0 : (j > i ? i : j);
-        const int k0 = j * kPBS;
-        if (k0 + kPBS <= L) {  // a whole block: scalar row offset
+        return j * kPBS;
+    };
+    // Global -> registers.  A whole block uses a scalar row offset; in the
+    // context's partial last block, rows past the end read the last token.
+    auto fetch_k = [&](int it) {
+        const int k0 = block_start(it);
+        if (k0 + kPBS <= L) {
             const uint32_t soff = (uint32_t)k0 * D * 2;
 #pragma unroll
             for (int c = 0; c < KCH; ++c) kreg[c] = buf_ld16(krs, koff[c], soff);
+        } else {
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int tok = k0 + krow[c] < L ? k0 + krow[c] : L - 1;
+                kreg[c] = buf_ld16(krs, (uint32_t)((tok - krow[c]) * D * 2) + koff[c], 0);
+            }
+        }
+    };
+    auto fetch_v = [&](int it) {
+        const int k0 = block_start(it);
+        if (k0 + kPBS <= L) {
+            const uint32_t soff = (uint32_t)k0 * D * 2;
 #pragma unroll
             for (int c = 0; c < VPR; ++c) {
                 vreg[c][0] = buf_ld16(vrs, voff[c], soff);
                 vreg[c][1] = buf_ld16(vrs, voff[c] + D * 2, soff);
             }
-        } else {  // the context's partial last block
-            auto clamped = [&](int r, uint32_t off) {
-                const int tok = k0 + r < L ? k0 + r : L - 1;
-                return (uint32_t)((tok - r) * D * 2) + off;
-            };
+        } else {
 #pragma unroll
-            for (int c = 0; c < KCH; ++c) kreg[c] = buf_ld16(krs, clamped(krow[c], koff[c]), 0);
+            for (int c = 0; c < VPR; ++c)
 #pragma unroll
-            for (int c = 0; c < VPR; ++c) {
-                vreg[c][0] = buf_ld16(vrs, clamped(vrow[c], voff[c]), 0);
-                vreg[c][1] = buf_ld16(vrs, clamped(vrow[c] + 1, voff[c] + D * 2), 0);
+                for (int u = 0; u < 2; ++u) {
+                    const int r = vrow[c] + u;
+                    const int tok = k0 + r < L ? k0 + r : L - 1;
+                    vreg[c][u] = buf_ld16(vrs, (uint32_t)((tok - r) * D * 2) + voff[c] + u * D * 2, 0);
+                }
+        }
+    };
+    auto store_k = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) *reinterpret_cast<uint4 *>(k_lds + buf * KBYTES + kst[c]) = kreg[c];
+    };
+    // S^T[key][qrow] of this wave's 32 keys and 32 rows: s[r][t] holds keys
+    // 32kh + 16t + 4g + e of query row qtok[r]; each K operand serves both tiles.
+    auto scores = [&](f32x4_t (&s)[2][2], int buf) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) s[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const char *krow_lds = k_lds + buf * KBYTES + (32 * kh + 16 * t + n) * (D * 2);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((g + 4 * ks) ^ n) << 4));
+#pragma unroll
+                for (int r = 0; r < 2; ++r) s[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[r][ks], s[r][t], 0, 0, 0);
             }
         }
     };
-    if (cnt > 0) fetch(0);
-
-    for (int it = 0; it < cnt; ++it) {
-        int j = block_of(it);
-        j = j < 0 ? 0 : (j > i ? i : j);
-        const int k0 = j * kPBS;
-        __syncthreads();  // previous block's LDS reads are done
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
-            *reinterpret_cast<uint4 *>(&k_lds[r * KPAD + cc * 8]) = kreg[c];
-        }
+    auto store_v = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < VPR; ++c) {
             const uint32_t a4[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
             const uint32_t b4[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                // (row 2rp, row 2rp+1) of column 2*e2, then of column 2*e2+1
+                // (row 2rp, row 2rp+1) of column 2*e2, then of column 2*e2+1 (the next V^T row)
                 const uint32_t lo = __builtin_amdgcn_perm(b4[e2], a4[e2], 0x05040100u);
                 const uint32_t hi = __builtin_amdgcn_perm(b4[e2], a4[e2], 0x07060302u);
-                *reinterpret_cast<uint32_t *>(vt_bytes + vst[c][2 * e2]) = lo;
-                *reinterpret_cast<uint32_t *>(vt_bytes + vst[c][2 * e2 + 1]) = hi;
+                *reinterpret_cast<uint32_t *>(vt_lds + buf * KBYTES + vst[c][e2]) = lo;
+                *reinterpret_cast<uint32_t *>(vt_lds + buf * KBYTES + vst[c][e2] + kPBS * 2) = hi;
             }
         }
-        __syncthreads();
-        if (it + 1 < cnt) fetch(it + 1);  // in flight while this block is computed
-
-        // S^T[key][qrow] for the 64 keys of block j, 16 at a time.
-        f32x4_t s[4];
+    };
+    // Causal / length masks: only the diagonal block and a partial last block need them.
+    auto is_edge = [&](int it) {
+        const int k0 = block_start(it);
+        return k0 == i * kPBS || k0 + kPBS > L;
+    };
+    auto mask = [&](f32x4_t (&s)[2][2], int it) {
+        const int k0 = block_start(it);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&k_lds[(16 * t + n) * KPAD + 8 * g + 32 * ks]);
-                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], s[t], 0, 0, 0);
-            }
-        }
-        // Lane holds keys 16t + 4g + e of query row qtok.  Only the diagonal block
-        // and a partial last block need the causal / length masks.
-        float mloc = -INFINITY;
-        if (j == i || k0 + kPBS > L) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int ktok = k0 + 16 * t + 4 * g + e;
-                    const float x = (ktok > qtok || ktok >= L) ? -INFINITY : s[t][e];
-                    s[t][e] = x;
-                    mloc = fmax_fast(mloc, x);
+                    const int ktok = k0 + 32 * kh + 16 * t + 4 * g + e;
+                    if (ktok > qtok[r] || ktok >= L) s[r][t][e] = -INFINITY;
                 }
-        } else {
+    };
+    // Running maximum with lazy rescaling: the reference m_run[r] moves only
+    // when the block's maximum exceeds it by more than kLazyRescale (log2
+    // units), so the weights stay below 2^kLazyRescale and O is rarely
+    // rescaled.  Any reference gives the same softmax once O is divided by l.
+    float m_ref[2] = {0.f, 0.f};
+    auto prep = [&](const f32x4_t (&s)[2][2], bool live) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+        for (int r = 0; r < 2; ++r) {
+            float mloc = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mloc = fmax_fast(mloc, s[t][e]);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mloc = fmax_fast(mloc, s[r][t][e]);
+            mloc = max_xor32(max_xor16(mloc)) * scale_log2;  // the 4 lanes of this query row; scale > 0
+            const bool bump = live && mloc > m_run[r] + kLazyRescale;  // always when m_run is still -inf
+            const float m_new = bump ? mloc : m_run[r];
+            const float ref = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = bump ? fast_exp2(m_run[r] - ref) : 1.0f;
+            m_run[r] = m_new;
+            m_ref[r] = ref;
+            l_run[r] *= alpha;
+            if (__ballot(bump)) {  // some row's reference moved
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[r][dt] *= alpha;
+            }
         }
-        mloc = max_xor32(max_xor16(mloc)) * scale_log2;  // the 4 lanes of this query row; scale > 0
-        const float m_new = fmax_fast(m_run, mloc);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_ref);
-        m_run = m_new;
-        float lsum = 0.f;
+    };
+    // Weights of one block (relative to m_ref) into the P^T operands:
+    // k-slots 8g..8g+3 <- keys 4g + e, 8g+4..8g+7 <- keys 16 + 4g + e (of the half).
+    auto weights = [&](f32x4_t (&s)[2][2], bf16x8_t (&pb)[2]) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int r = 0; r < 2; ++r) {
+            float lsum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = fast_exp2(fmaf(s[r][t][e], scale_log2, -m_ref[r]));
+                    s[r][t][e] = p;
+                    lsum += p;
+                }
+            l_run[r] += lsum;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = fast_exp2(fmaf(s[t][e], scale_log2, -m_ref));
-                s[t][e] = p;
-                lsum += p;
+                pb[r][e] = (__bf16)s[r][0][e];
+                pb[r][4 + e] = (__bf16)s[r][1][e];
             }
-        l_run = l_run * alpha + lsum;
-        if (__ballot(alpha != 1.0f)) {  // some row's maximum moved
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         }
-        // P^T operand: k-slots 8g..8g+3 <- keys 32ks + 4g + e, 8g+4..8g+7 <- keys 32ks + 16 + 4g + e.
-        bf16x8_t pb[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pb[ks][e] = (__bf16)s[2 * ks][e];
-                pb[ks][4 + e] = (__bf16)s[2 * ks + 1][e];
-            }
+    };
+    auto pv = [&](const bf16x8_t (&pb)[2], int buf) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const int dcol = 16 * dt + n;
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(vt_lds + buf * KBYTES + dcol * (kPBS * 2) +
+                                                                    (vt_group_pos(dcol, 4 * kh + g) << 4));
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int sg = 4 * ks + g;
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                    vt_bytes + dcol * (kPBS * 2) + ((sg ^ ((dcol ^ (dcol >> 3)) & 7)) << 4));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], oacc[dt], 0, 0, 0);
-            }
+            for (int r = 0; r < 2; ++r) oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[r], oacc[r][dt], 0, 0, 0);
         }
+    };
+
+    // Software pipeline over double-buffered LDS.  Iteration it computes the
+    // scores of block it + 1 and P V of block it (MFMA) alongside the weights of
+    // block it (VALU), then masks block it + 1 if it is an edge block and takes
+    // its maximum.  At its start it stores K of block it + 2 and V of block
+    // it + 1 (fetched one iteration earlier) into the buffers freed by the last
+    // iteration and issues the loads for the next; one barrier per iteration.
+    // Buffer parity follows it, so the loop is unrolled by two.
+    f32x4_t sA[2][2], sB[2][2];
+    if (cnt > 0) {
+        fetch_k(0);
+        fetch_v(0);
+        store_k(0);
+        store_v(0);
+        if (cnt > 1) {
+            fetch_k(1);
+            store_k(1);
+        }
+        __syncthreads();
+        if (cnt > 2) fetch_k(2);
+        if (cnt > 1) fetch_v(1);
+        scores(sA, 0);
+        if (is_edge(0)) mask(sA, 0);
+        prep(sA, true);
+        __syncthreads();  // block 0's K buffer is free
+    }
+    // s_cur holds block it's masked scores with its reference applied to O and
+    // l; s_next receives block it + 1.  P = it & 1 (compile-time).
+    auto step = [&](auto par, int it, f32x4_t (&s_cur)[2][2], f32x4_t (&s_next)[2][2]) {
+        constexpr int P = decltype(par)::value;
+        const bool has_next = it + 1 < cnt;
+        if (it + 2 < cnt) store_k(P);      // K of block it + 2 where block it's was
+        if (has_next) store_v(1 - P);      // V of block it + 1 where block it - 1's was
+        if (it + 3 < cnt) fetch_k(it + 3);
+        if (it + 2 < cnt) fetch_v(it + 2);
+        // One straight-line region (no branch inside) so that the MFMAs of the
+        // scores and of P V interleave with the VALU work on the weights.
+        bf16x8_t pb[2];
+        scores(s_next, 1 - P);  // on the last step this recomputes block it's scores: unused
+        weights(s_cur, pb);
+        pv(pb, P);
+        if (has_next && is_edge(it + 1)) mask(s_next, it + 1);
+        prep(s_next, has_next);
+        __syncthreads();  // stores visible; reads of this iteration's buffers done
+    };
+    for (int it = 0; it < cnt; it += 2) {
+        step(std::integral_constant<int, 0>{}, it, sA, sB);
+        if (it + 1 >= cnt) break;
+        step(std::integral_constant<int, 1>{}, it + 1, sB, sA);
     }
 
-    const float l_tot = sum_xor32(sum_xor16(l_run));
-    if (qtok < L) {
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        uint16_t *orow = out + head + (int64_t)qtok * D;
+    // Merge the two key halves of each row: the kh = 1 waves hand (m, l, O) to
+    // their kh = 0 partners through LDS.
+    float l_row[2];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const uint32_t w0 = (uint32_t)f32_to_bf16(oacc[dt][0] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][1] * inv) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16(oacc[dt][2] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][3] * inv) << 16);
-            *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = make_uint2(w0, w1);
+    for (int r = 0; r < 2; ++r) l_row[r] = sum_xor32(sum_xor16(l_run[r]));
+    float *xo = reinterpret_cast<float *>(smem);
+    __syncthreads();  // the staging area is free
+    if (kh == 1) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(xo + ((rh * 2 + r) * DT + dt) * 256 + lane * 4) = oacc[r][dt];
+            xml[rh][r][0][lane] = m_run[r];
+            xml[rh][r][1][lane] = l_row[r];
         }
-        if (g == 0 && lse) lse[((int64_t)b * H + h) * L + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    float lse2[2];  // final log2-domain row log-sum-exp (kh = 0 waves)
+    if (kh == 0) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float m1 = xml[rh][r][0][lane], l1 = xml[rh][r][1][lane];
+            const float m = fmax_fast(m_run[r], m1);
+            const float m_ref = m == -INFINITY ? 0.f : m;
+            const float a0 = fast_exp2(m_run[r] - m_ref), a1 = fast_exp2(m1 - m_ref);
+            const float l_tot = l_row[r] * a0 + l1 * a1;
+            lse2[r] = l_tot > 0.f ? m + log2f(l_tot) : INFINITY;
+            if (qtok[r] < L) {
+                const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+                uint16_t *orow = out + head + (int64_t)qtok[r] * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + ((rh * 2 + r) * DT + dt) * 256 + lane * 4);
+                    const f32x4_t o = (oacc[r][dt] * a0 + o1 * a1) * inv;
+                    const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+                    const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+                    *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = make_uint2(w0, w1);
+                }
+                if (g == 0 && lse) lse[((int64_t)b * H + h) * L + qtok[r]] = l_tot > 0.f ? lse2[r] * kLn2 : -INFINITY;
+            }
+        }
     }
     if constexpr (GT) {
         // Second sweep: each block's share of every row's softmax, averaged over the block's rows.
+        __shared__ float row_lse2[64];
         __shared__ float red[4];
-        const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : INFINITY;
+        if (kh == 0) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                if (g == 0) row_lse2[32 * rh + 16 * r + n] = lse2[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 2; ++r) lse2[r] = row_lse2[32 * rh + 16 * r + n];
         const int rows_i = L - i * kPBS < kPBS ? L - i * kPBS : kPBS;
         float *mrow = mass + row * nb;
-        for (int j = i + 1 + tid; j < nb; j += 256) mrow[j] = 0.f;
-        for (int j = 0; j <= i; ++j) {
-            const int k0 = j * kPBS;
+        for (int jj = i + 1 + tid; jj < nb; jj += 256) mrow[jj] = 0.f;
+        for (int jb = 0; jb <= i; ++jb) {
+            const int k0 = jb * kPBS;
+            fetch_k(jb);
             __syncthreads();  // previous readers of k_lds and red are done
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
-                const int tok = k0 + r;
-                const uint4 w = tok < L ? *reinterpret_cast<const uint4 *>(kh + (int64_t)tok * D + cc * 8)
-                                        : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(&k_lds[r * KPAD + cc * 8]) = w;
-            }
+            store_k(0);
             __syncthreads();
+            f32x4_t s[2][2];
+            scores(s, 0);
             float psum = 0.f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&k_lds[(16 * t + n) * KPAD + 8 * g + 32 * ks]);
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], st, 0, 0, 0);
-                }
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ktok = k0 + 16 * t + 4 * g + e;
-                    const bool live = ktok <= qtok && ktok < L && qtok < L;
-                    psum += live ? fast_exp2(st[e] * scale_log2 - lse2) : 0.f;
-                }
-            }
+                    for (int e = 0; e < 4; ++e) {
+                        const int ktok = k0 + 32 * kh + 16 * t + 4 * g + e;
+                        const bool live = ktok <= qtok[r] && ktok < L && qtok[r] < L;
+                        psum += live ? fast_exp2(s[r][t][e] * scale_log2 - lse2[r]) : 0.f;
+                    }
             psum = wave_sum(psum);
             if (lane == 0) red[wave] = psum;
             __syncthreads();
-            if (tid == 0) mrow[j] = (red[0] + red[1] + red[2] + red[3]) / (float)rows_i;
+            if (tid == 0) mrow[jb] = (red[0] + red[1] + red[2] + red[3]) / (float)rows_i;
         }
     }
 }
