@@ -217,20 +217,15 @@ __global__ __launch_bounds__(256) void prefill_select_rows_kernel(const float *S
 // waves instead of four; the two key halves of a row are merged once at the end
 // (their running maxima and sums combine as in split-KV decoding).
 //
-// LDS layouts (one 64-key block; bank behaviour measured on gfx950):
-//  K   : key rows of 256 bytes, 16-byte chunk c of key r stored at chunk
-//        c ^ (r & 15), so the 16 keys x 16 bytes of an MFMA A operand, and the
-//        8-lane groups of the staging writes, hit distinct banks.
-//  V^T : d rows of 128 bytes holding the 64 keys as 8 groups of 8 (16 bytes);
-//        group sg = 4 * (key >> 5) + ((key >> 2) & 3) lists keys in the order
-//        lane (g, n) supplies k-slots 8g..8g+7 of P^T (key & 3, then bit 4),
-//        and sits at position sg ^ (((d >> 1) ^ (d >> 4)) & 7) of its row.
-__device__ __forceinline__ int vt_group_pos(int d, int sg) { return (sg ^ ((d >> 1) ^ (d >> 4))) & 7; }
-__device__ __forceinline__ int vt_byte(int d, int key) {
-    const int sg = 4 * (key >> 5) + ((key >> 2) & 3);
-    const int slot = (key & 3) + (((key >> 4) & 1) << 2);
-    return d * (kPBS * 2) + (vt_group_pos(d, sg) << 4) + slot * 2;
-}
+// LDS layouts (one 64-key block of 256-byte rows; bank behaviour measured on
+// gfx950).  Both are filled by buffer_load ... lds, which writes lane l's 16
+// bytes at the wave's LDS base + 16 l, so a swizzle is a choice of which
+// global chunk each lane loads.
+//  K : 16-byte chunk c of key r at chunk c ^ (r & 15): the 16 keys x 16 bytes
+//      of an MFMA A operand read hit distinct banks.
+//  V : 32-byte chunk c (columns 16c..16c+15) of key r at chunk c ^ (r & 7):
+//      the transposing reads (ds_read_b64_tr_b16) that build the V^T operand
+//      from 16 keys x 32 bytes hit distinct banks.
 
 // GT (the ground-truth form): every causal block j <= i is attended (the lists
 // are not read), and after the output a second sweep over K recomputes the
@@ -247,15 +242,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     constexpr int KS = D / 32;           // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;           // 16-wide d tiles of O^T
     constexpr int CPR = D / 8;           // 16-byte chunks per key row
-    constexpr int KCH = kPBS * CPR / 256;        // K chunks staged per thread
-    constexpr int VPR = (kPBS / 2) * CPR / 256;  // V (row pair, chunk) items per thread
     constexpr int KBYTES = kPBS * D * 2;
-    // Two K buffers, then two V^T buffers during the sweep; the key-half
-    // exchange (2 waves x 2 tiles x DT x 256 floats) after it.
-    __shared__ __align__(16) char smem[4 * KBYTES];
+    constexpr int DMA_PER_WAVE = KBYTES / 1024 / 4;  // 1 KiB buffer_load ... lds per wave and tensor
+    // Two K and two V buffers (separate objects, so that the compiler sees a load
+    // into one buffer does not alias reads of another); the key-half exchange
+    // (2 tiles x DT x 256 floats per row half) reuses the K buffers after the sweep.
+    __shared__ __align__(16) char kbuf0[KBYTES], kbuf1[KBYTES], vbuf0[KBYTES], vbuf1[KBYTES];
     __shared__ float xml[2][2][2][64];   // [rh][tile][m | l][lane] of the key-half-1 waves
-    static_assert(2 * 2 * DT * 256 * 4 <= 2 * KBYTES, "exchange fits the staging area");
-    char *const k_lds = smem, *const vt_lds = smem + 2 * KBYTES;  // buffer b at + b * KBYTES
+    static_assert(2 * DT * 256 * 4 <= KBYTES, "one row half's exchange fits a K buffer");
 
     // Workgroups reach the 8 XCDs round-robin (id % 8); give each XCD one
     // contiguous range of the (b, h)-major list so that a head's K / V blocks
@@ -297,115 +291,61 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     const int64_t row = ((int64_t)b * H + h) * nb + i;
     int cnt = GT ? i + 1 : kv_count[row];
     cnt = cnt < 0 ? 0 : (cnt > kmax_row ? kmax_row : cnt);
-    const int32_t *blist = GT ? nullptr : kv_blocks + row * kmax_row;
+    // The lists are read-only here: read them through the constant address
+    // space so that they are scalar loads, which do not wait behind the
+    // in-flight K / V loads the way a vector load's vmcnt would.
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const_i32 *blist = GT ? nullptr : (const_i32 *)(kv_blocks + row * kmax_row);
     auto block_of = [&](int it) { return GT ? it : blist[it]; };
 
-    // K and V of the head through buffer descriptors: a block's first row is a
-    // scalar byte offset, each thread's chunks fixed 32-bit offsets.  In the
-    // last block of a context that is not a multiple of 64, rows past the end
-    // read the last token instead (their scores are masked, their weights 0).
+    // K and V of the head through buffer descriptors, loaded straight into LDS.
+    // Wave w fills rows 16w..16w+15 of a buffer, 4 rows (1 KiB) per load; lane
+    // l takes row 16w + 4q + l / 16 and the global chunk whose swizzled slot is
+    // l % 16.  In the last block of a context that is not a multiple of 64,
+    // rows past the end read the last token (their scores are masked).
     const uint32_t head_bytes = (uint32_t)((int64_t)L * D * 2);
     const auto krs = buffer_rsrc(kh_ptr, head_bytes), vrs = buffer_rsrc(vh, head_bytes);
-    uint32_t koff[KCH], kst[KCH], voff[VPR];
-    int krow[KCH], vrow[VPR];
+    uint32_t kdv[DMA_PER_WAVE], vdv[DMA_PER_WAVE];
+    int drow[DMA_PER_WAVE];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-        const int ch = tid + 256 * c, r = ch / CPR, cc = ch % CPR;
-        krow[c] = r;
-        koff[c] = (uint32_t)(r * D * 2 + cc * 16);
-        kst[c] = (uint32_t)(r * D * 2 + ((cc ^ (r & 15)) << 4));
+    for (int qd = 0; qd < DMA_PER_WAVE; ++qd) {
+        const int r = 16 * wave + 4 * qd + (lane >> 4), s = lane & 15;
+        drow[qd] = r;
+        kdv[qd] = (uint32_t)(r * D * 2 + ((s ^ (r & 15)) << 4));
+        vdv[qd] = (uint32_t)(r * D * 2 + (((((s >> 1) ^ (r & 7)) << 1) | (s & 1)) << 4));
     }
-    // V items: lane bits 0-2 pick the 16-byte column chunk, bit 3 row-pair bit 0,
-    // bit 4 row-pair bit 3, bit 5 chunk bit 3; the wave gives row-pair bits 1-2 and
-    // the item index bit 4.  With the V^T layout above every 32-lane half of each
-    // 4-byte store then covers the 32 banks once.
-    uint32_t vst[VPR][4];
-#pragma unroll
-    for (int c = 0; c < VPR; ++c) {
-        const int cc = (lane & 7) + 8 * (lane >> 5);
-        const int rp = ((lane >> 3) & 1) + 2 * (wave & 1) + 4 * (wave >> 1) + 8 * ((lane >> 4) & 1) + 16 * c;
-        vrow[c] = 2 * rp;
-        voff[c] = (uint32_t)(vrow[c] * D * 2 + cc * 16);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) vst[c][e2] = (uint32_t)vt_byte(cc * 8 + 2 * e2, vrow[c]);
-    }
-
-    uint4 kreg[KCH], vreg[VPR][2];
     auto block_start = [&](int it) {
         int j = block_of(it);
         j = j < 0 ? 0 : (j > i ? i : j);
         return j * kPBS;
     };
-    // Global -> registers.  A whole block uses a scalar row offset; in the
-    // context's partial last block, rows past the end read the last token.
-    auto fetch_k = [&](int it) {
+    auto dma = [&](int it, char *dst, __amdgpu_buffer_rsrc_t rs, const uint32_t (&dv)[DMA_PER_WAVE]) {
         const int k0 = block_start(it);
-        if (k0 + kPBS <= L) {
-            const uint32_t soff = (uint32_t)k0 * D * 2;
+        char *base = dst + wave * (DMA_PER_WAVE * 1024);
+        const int last = L - 1 - k0;  // rows past it (partial last block) read the last token
 #pragma unroll
-            for (int c = 0; c < KCH; ++c) kreg[c] = buf_ld16(krs, koff[c], soff);
-        } else {
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const int tok = k0 + krow[c] < L ? k0 + krow[c] : L - 1;
-                kreg[c] = buf_ld16(krs, (uint32_t)((tok - krow[c]) * D * 2) + koff[c], 0);
-            }
+        for (int qd = 0; qd < DMA_PER_WAVE; ++qd) {
+            const int over = drow[qd] - last;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(base + qd * 1024), 16,
+                                                     (int)dv[qd] - (over > 0 ? over : 0) * D * 2, k0 * D * 2, 0, 0);
         }
     };
-    auto fetch_v = [&](int it) {
-        const int k0 = block_start(it);
-        if (k0 + kPBS <= L) {
-            const uint32_t soff = (uint32_t)k0 * D * 2;
-#pragma unroll
-            for (int c = 0; c < VPR; ++c) {
-                vreg[c][0] = buf_ld16(vrs, voff[c], soff);
-                vreg[c][1] = buf_ld16(vrs, voff[c] + D * 2, soff);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < VPR; ++c)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int r = vrow[c] + u;
-                    const int tok = k0 + r < L ? k0 + r : L - 1;
-                    vreg[c][u] = buf_ld16(vrs, (uint32_t)((tok - r) * D * 2) + voff[c] + u * D * 2, 0);
-                }
-        }
-    };
-    auto store_k = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) *reinterpret_cast<uint4 *>(k_lds + buf * KBYTES + kst[c]) = kreg[c];
-    };
+    auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's loads are in LDS
     // S^T[key][qrow] of this wave's 32 keys and 32 rows: s[r][t] holds keys
     // 32kh + 16t + 4g + e of query row qtok[r]; each K operand serves both tiles.
-    auto scores = [&](f32x4_t (&s)[2][2], int buf) {
+    auto scores = [&](f32x4_t (&s)[2][2], const char *kb) {
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int t = 0; t < 2; ++t) s[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const char *krow_lds = k_lds + buf * KBYTES + (32 * kh + 16 * t + n) * (D * 2);
+            const char *krow_lds = kb + (32 * kh + 16 * t + n) * (D * 2);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((g + 4 * ks) ^ n) << 4));
 #pragma unroll
                 for (int r = 0; r < 2; ++r) s[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[r][ks], s[r][t], 0, 0, 0);
-            }
-        }
-    };
-    auto store_v = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < VPR; ++c) {
-            const uint32_t a4[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
-            const uint32_t b4[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                // (row 2rp, row 2rp+1) of column 2*e2, then of column 2*e2+1 (the next V^T row)
-                const uint32_t lo = __builtin_amdgcn_perm(b4[e2], a4[e2], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(b4[e2], a4[e2], 0x07060302u);
-                *reinterpret_cast<uint32_t *>(vt_lds + buf * KBYTES + vst[c][e2]) = lo;
-                *reinterpret_cast<uint32_t *>(vt_lds + buf * KBYTES + vst[c][e2] + kPBS * 2) = hi;
             }
         }
     };
@@ -475,12 +415,21 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
             }
         }
     };
-    auto pv = [&](const bf16x8_t (&pb)[2], int buf) {
+    // V^T operand of d tile dt: two transposing reads giving keys
+    // 32kh + 16h + 4g + e (h = 0, 1; e = 0..3) of column 16dt + n, the k-slot
+    // order of P^T.  Lane (g, s) points at row 32kh + 4g + s / 4 (+ 16 for h = 1),
+    // columns 16dt + 4 (s % 4) + 0..3; rows 32kh + 4g + s / 4 and + 16 share r & 7.
+    const int vrow_rd = 32 * kh + 4 * g + (n >> 2), vx = vrow_rd & 7;
+    auto pv = [&](const bf16x8_t (&pb)[2], const char *vb) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const char *vr = vb + vrow_rd * (D * 2) + (n & 3) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const int dcol = 16 * dt + n;
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(vt_lds + buf * KBYTES + dcol * (kPBS * 2) +
-                                                                    (vt_group_pos(dcol, 4 * kh + g) << 4));
+            const char *p = vr + ((dt ^ vx) << 5);
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s *)(p + 16 * D * 2));
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int r = 0; r < 2; ++r) oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[r], oacc[r][dt], 0, 0, 0);
         }
@@ -489,24 +438,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // Software pipeline over double-buffered LDS.  Iteration it computes the
     // scores of block it + 1 and P V of block it (MFMA) alongside the weights of
     // block it (VALU), then masks block it + 1 if it is an edge block and takes
-    // its maximum.  At its start it stores K of block it + 2 and V of block
-    // it + 1 (fetched one iteration earlier) into the buffers freed by the last
-    // iteration and issues the loads for the next; one barrier per iteration.
-    // Buffer parity follows it, so the loop is unrolled by two.
+    // its maximum.  At its start it issues the loads of K of block it + 2 and V
+    // of block it + 1 into the buffers the last iteration finished with; they
+    // land while it computes.  One barrier per iteration.  Buffer parity follows
+    // it, so the loop is unrolled by two.
     f32x4_t sA[2][2], sB[2][2];
     if (cnt > 0) {
-        fetch_k(0);
-        fetch_v(0);
-        store_k(0);
-        store_v(0);
-        if (cnt > 1) {
-            fetch_k(1);
-            store_k(1);
-        }
+        dma(0, kbuf0, krs, kdv);
+        dma(0, vbuf0, vrs, vdv);
+        if (cnt > 1) dma(1, kbuf1, krs, kdv);
+        loads_done();
         __syncthreads();
-        if (cnt > 2) fetch_k(2);
-        if (cnt > 1) fetch_v(1);
-        scores(sA, 0);
+        scores(sA, kbuf0);
         if (is_edge(0)) mask(sA, 0);
         prep(sA, true);
         __syncthreads();  // block 0's K buffer is free
@@ -515,20 +458,21 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // l; s_next receives block it + 1.  P = it & 1 (compile-time).
     auto step = [&](auto par, int it, f32x4_t (&s_cur)[2][2], f32x4_t (&s_next)[2][2]) {
         constexpr int P = decltype(par)::value;
+        char *const k_this = P ? kbuf1 : kbuf0, *const k_next = P ? kbuf0 : kbuf1;
+        char *const v_this = P ? vbuf1 : vbuf0, *const v_next = P ? vbuf0 : vbuf1;
         const bool has_next = it + 1 < cnt;
-        if (it + 2 < cnt) store_k(P);      // K of block it + 2 where block it's was
-        if (has_next) store_v(1 - P);      // V of block it + 1 where block it - 1's was
-        if (it + 3 < cnt) fetch_k(it + 3);
-        if (it + 2 < cnt) fetch_v(it + 2);
+        if (it + 2 < cnt) dma(it + 2, k_this, krs, kdv);  // where block it's K was
+        if (has_next) dma(it + 1, v_next, vrs, vdv);       // where block it - 1's V was
         // One straight-line region (no branch inside) so that the MFMAs of the
         // scores and of P V interleave with the VALU work on the weights.
         bf16x8_t pb[2];
-        scores(s_next, 1 - P);  // on the last step this recomputes block it's scores: unused
+        scores(s_next, k_next);  // on the last step this reads a stale buffer: unused
         weights(s_cur, pb);
-        pv(pb, P);
+        pv(pb, v_this);
         if (has_next && is_edge(it + 1)) mask(s_next, it + 1);
         prep(s_next, has_next);
-        __syncthreads();  // stores visible; reads of this iteration's buffers done
+        loads_done();
+        __syncthreads();  // loads visible; reads of this iteration's buffers done
     };
     for (int it = 0; it < cnt; it += 2) {
         step(std::integral_constant<int, 0>{}, it, sA, sB);
@@ -541,14 +485,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     float l_row[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) l_row[r] = sum_xor32(sum_xor16(l_run[r]));
-    float *xo = reinterpret_cast<float *>(smem);
+    float *xo = reinterpret_cast<float *>(rh ? kbuf1 : kbuf0);  // per row half: 2 tiles x DT x 256 floats
     __syncthreads();  // the staging area is free
     if (kh == 1) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4_t *>(xo + ((rh * 2 + r) * DT + dt) * 256 + lane * 4) = oacc[r][dt];
+                *reinterpret_cast<f32x4_t *>(xo + (r * DT + dt) * 256 + lane * 4) = oacc[r][dt];
             xml[rh][r][0][lane] = m_run[r];
             xml[rh][r][1][lane] = l_row[r];
         }
@@ -569,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                 uint16_t *orow = out + head + (int64_t)qtok[r] * D;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + ((rh * 2 + r) * DT + dt) * 256 + lane * 4);
+                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + (r * DT + dt) * 256 + lane * 4);
                     const f32x4_t o = (oacc[r][dt] * a0 + o1 * a1) * inv;
                     const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
                     const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
@@ -596,12 +540,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         for (int jj = i + 1 + tid; jj < nb; jj += 256) mrow[jj] = 0.f;
         for (int jb = 0; jb <= i; ++jb) {
             const int k0 = jb * kPBS;
-            fetch_k(jb);
-            __syncthreads();  // previous readers of k_lds and red are done
-            store_k(0);
+            __syncthreads();  // previous readers of the K buffer and red are done
+            dma(jb, kbuf0, krs, kdv);
+            loads_done();
             __syncthreads();
             f32x4_t s[2][2];
-            scores(s, 0);
+            scores(s, kbuf0);
             float psum = 0.f;
 #pragma unroll
             for (int r = 0; r < 2; ++r)
