@@ -322,12 +322,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     auto dma = [&](int it, char *dst, __amdgpu_buffer_rsrc_t rs, const uint32_t (&dv)[DMA_PER_WAVE]) {
         const int k0 = block_start(it);
         char *base = dst + wave * (DMA_PER_WAVE * 1024);
-        const int last = L - 1 - k0;  // rows past it (partial last block) read the last token
+        if (k0 + kPBS <= L) {  // a whole block: the row offset is scalar
 #pragma unroll
-        for (int qd = 0; qd < DMA_PER_WAVE; ++qd) {
-            const int over = drow[qd] - last;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(base + qd * 1024), 16,
-                                                     (int)dv[qd] - (over > 0 ? over : 0) * D * 2, k0 * D * 2, 0, 0);
+            for (int qd = 0; qd < DMA_PER_WAVE; ++qd)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(base + qd * 1024),
+                                                         16, (int)dv[qd], k0 * D * 2, 0, 0);
+        } else {  // the context's partial last block
+#pragma unroll
+            for (int qd = 0; qd < DMA_PER_WAVE; ++qd) {
+                const int over = drow[qd] - (L - 1 - k0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(base + qd * 1024),
+                                                         16, (int)dv[qd] - (over > 0 ? over : 0) * D * 2, k0 * D * 2, 0, 0);
+            }
         }
     };
     auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's loads are in LDS
@@ -386,10 +392,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
             const float alpha = bump ? fast_exp2(m_run[r] - ref) : 1.0f;
             m_run[r] = m_new;
             m_ref[r] = ref;
-            l_run[r] *= alpha;
             if (__ballot(bump)) {  // some row's reference moved
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) oacc[r][dt] *= alpha;
+                l_run[r] *= alpha;
             }
         }
     };
