@@ -13,22 +13,24 @@
 //
 // gfx950 design.  One workgroup (4 waves) per (split, KV head, sequence).  A
 // split owns a contiguous range of "units" (a kept block, or the tail).  For
-// every unit each wave takes a quarter of the block's tokens:
-//   loads : non-temporal 16-byte buffer loads; the unit's first row is a
-//        scalar offset, each lane's rows a fixed 32-bit offset, and rows past
-//        the cache read as zero (the descriptor's range check).
-//   QK : 8 lanes per key row, each lane a 16-byte chunk per 64 head dims;
-//        v_dot2_f32_bf16 with the bf16 query held in registers, then an
-//        8-lane DPP all-reduce.  The key bytes feed all G query heads.
+// every unit each wave takes a quarter of the block's tokens (32 or 16) and
+// does both products on v_mfma_f32_16x16x{32,16}_bf16 with the group's query
+// heads as the 16-wide N dimension (G <= 8 of them used):
+//   QK : S^T = K Q^T.  Each lane loads its 16-byte pieces of the K operand
+//        straight from HBM (non-temporal buffer loads; the unit's first row is
+//        a scalar offset, rows past the cache read as zero); the bf16 query
+//        is a register operand.  Lane (g4, n) gets head n's scores of tokens
+//        16t + 4 g4 + 0..3, which is exactly its slice of the P^T operand.
 //   softmax : log2 domain, the scale folded into one FMA; one running max
-//        per head that is uniform across the wave, so partial sums need no
-//        rescaling when the wave's lane groups are combined, and the
-//        accumulators are rescaled only when some head's maximum moved.
-//   PV : probabilities go through LDS to a second layout, one 16-byte value
-//        chunk per lane (a whole 256-byte row per 16 lanes, fully coalesced),
-//        fp32 FMA into G x 8 accumulators per lane.
-// At the end the wave's lane groups and then the 4 waves are combined, and
-// the split writes (unnormalised o, running max, running sum) per head -- or,
+//        per head, the same in the 4 lanes of the head, accumulators rescaled
+//        only when some head's maximum moved.
+//   PV : O^T = V^T P^T.  The wave's V rows go straight into its LDS tile
+//        (buffer_load ... lds, 32-byte chunks XOR-swizzled by row) and the V^T
+//        operand is read with ds_read_b64_tr_b16.  P is split into bf16 high
+//        and low parts (two MFMAs), so the products keep ~16 bits of the fp32
+//        weights.
+// At the end each wave's heads and then the 4 waves are combined, and the
+// split writes (unnormalised o, running max, running sum) per head -- or,
 // with a single split, the final normalised output directly.  A merge of the
 // splits by log-sum-exp follows (a second kernel, or later work items of the
 // fused step).
@@ -41,6 +43,10 @@
 #include <math.h>
 
 namespace seer {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
     const uint16_t *q;
@@ -76,16 +82,7 @@ __host__ __device__ inline int heads_union_words(int nb_max, int G, int k_max) {
 template <int D, int BS, int G>
 struct DecodeCfg {
     static constexpr int NT = 256, NW = 4;
-    static constexpr int CH = D / 8;          // 16-byte chunks per row
-    static constexpr int LPR = 8;             // QK: lanes per key row
-    static constexpr int ROWS = 64 / LPR;     // key rows per wave-wide load
-    static constexpr int CPL = CH / LPR;      // key chunks per lane
-    static constexpr int TPW = BS / NW;       // tokens per wave per unit
-    static constexpr int TPL = TPW / ROWS;    // key rows per lane per unit
-    static constexpr int LPV = CH;            // PV: lanes per value row (one chunk each)
-    static constexpr int ROWSV = 64 / LPV;    // value rows per wave-wide load
-    static constexpr int TPLV = TPW / ROWSV;  // value rows per lane per unit
-    static_assert(CPL >= 1 && TPL >= 1 && TPLV >= 1, "tile shape");
+    static constexpr int TPW = BS / NW;  // tokens per wave per unit
 };
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -101,12 +98,12 @@ __device__ __forceinline__ void store_out(void *out, int dtype, int64_t i, float
         static_cast<uint16_t *>(out)[i] = f32_to_bf16(x);
 }
 
-// LDS of one split: probabilities handed from the QK to the PV layout, and the
-// per-wave partial results combined at the end.
+// LDS of one split: each wave's V rows of the current unit, and the per-wave
+// partial results combined at the end.
 template <int D, int BS, int G>
 struct DecodeSmem {
     using C = DecodeCfg<D, BS, G>;
-    float p[C::NW][C::TPW][G];
+    __attribute__((aligned(16))) uint16_t vt[C::NW][C::TPW * D];
     float o[C::NW][G][D];
     float m[C::NW][G], l[C::NW][G];
     int n_union;  // per-head form: size of the group's union of kept blocks
@@ -125,9 +122,6 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
                                                   DecodeSmem<D, BS, G> &sm, uint32_t *dyn = nullptr) {
     using C = DecodeCfg<D, BS, G>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane / C::LPR, c = lane % C::LPR;      // QK layout
-    const int rv = lane / C::LPV, cv = lane % C::LPV;    // PV layout
-    auto &p_lds = sm.p;
     auto &sm_o = sm.o;
     auto &sm_m = sm.m;
     auto &sm_l = sm.l;
@@ -196,22 +190,24 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     const int u0 = (int)(((int64_t)split * units) / a.num_splits);
     const int u1 = (int)(((int64_t)(split + 1) * units) / a.num_splits);
 
-    // Query rows of the group, bf16 pairs, the chunks this lane multiplies.
-    uint4 qv[G][C::CPL];
+    constexpr int TPW = C::TPW;   // tokens per wave per unit: 32 or 16
+    constexpr int NKT = TPW / 16;  // 16-token tiles per wave
+    constexpr int KS = D / 32;     // k-steps of S^T = K Q^T
+    constexpr int DT = D / 16;     // 16-wide d tiles of O^T
+    constexpr int CPR = D / 8;     // 16-byte chunks per row
+    constexpr int RPD = 64 / CPR;  // rows per 1 KiB LDS load
+    constexpr int NDMA = TPW / RPD;
+    constexpr int XM = CPR / 2 - 1;  // 32-byte chunk swizzle mask
+    static_assert(G <= 16 && (TPW == 16 || TPW == 32), "MFMA decode tile");
+    const int g4 = lane >> 4, n = lane & 15;
+    const int wt0 = wave * TPW;  // first token of this wave inside a unit
+
+    // Q operand: lane (g4, n) holds dims 8 g4 + 32 ks .. + 7 of head n (zero for n >= G).
+    bf16x8_t qop[KS];
     const uint16_t *qb = a.q + b * a.sq_b + (int64_t)(g * G) * a.sq_h;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < C::CPL; ++i) qv[h][i] = ldg16(qb + h * a.sq_h + (c + i * C::LPR) * 8);
-
-    float m_run[G], l_part[G], o[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m_run[h] = -INFINITY;
-        l_part[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-    }
+    for (int ks = 0; ks < KS; ++ks)
+        qop[ks] = __builtin_bit_cast(bf16x8_t, n < G ? ldg16(qb + n * a.sq_h + 8 * g4 + 32 * ks) : make_uint4(0, 0, 0, 0));
 
     // K/V of (b, g) through buffer descriptors: a unit's first row is a scalar
     // byte offset, each lane's rows and chunks a fixed 32-bit offset.
@@ -221,15 +217,30 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, kBufferFlags);
     const int32_t *sel = (GT || PH) ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
-    const int wt0 = wave * C::TPW;  // first token of this wave inside a unit
-    uint32_t koff[C::TPL][C::CPL], voff[C::TPLV];
+    uint32_t kof[NKT][KS], vof[NDMA];
 #pragma unroll
-    for (int t = 0; t < C::TPL; ++t)
+    for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int i = 0; i < C::CPL; ++i)
-            koff[t][i] = (uint32_t)(((wt0 + r + t * C::ROWS) * a.skv_t + (c + i * C::LPR) * 8) * 2);
+        for (int ks = 0; ks < KS; ++ks)
+            kof[t][ks] = (uint32_t)(((wt0 + 16 * t + n) * a.skv_t + 8 * g4 + 32 * ks) * 2);
+    // V tile: lane l of load q fills LDS row rr = q RPD + l / CPR, 16-byte slot s = l % CPR,
+    // with the row's 16-byte chunk whose 32-byte half-pair lands there under the swizzle.
 #pragma unroll
-    for (int t = 0; t < C::TPLV; ++t) voff[t] = (uint32_t)(((wt0 + rv + t * C::ROWSV) * a.skv_t + cv * 8) * 2);
+    for (int q = 0; q < NDMA; ++q) {
+        const int rr = q * RPD + lane / CPR, s = lane % CPR;
+        const int c16 = ((((s >> 1) ^ (rr & XM)) << 1) | (s & 1));
+        vof[q] = (uint32_t)(((wt0 + rr) * a.skv_t + c16 * 8) * 2);
+    }
+    char *const vt = reinterpret_cast<char *>(sm.vt[wave]);
+    // Transposing reads: lane (g4, s) points at tile row 16t + 4 g4 + s / 4,
+    // columns 16 dt + 4 (s % 4) + 0..3; the row's swizzle does not depend on t.
+    const int trow = 4 * g4 + (n >> 2), tx = trow & XM;
+    const char *const vr0 = vt + trow * (D * 2) + (n & 3) * 8;
+
+    f32x4_t oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_part = 0.f;  // of head n
 
     int ids = 0, id0 = u0 - 64;  // kept block ids of units [id0, id0 + 64), one per lane
     for (int u = u0; u < u1; ++u) {
@@ -256,134 +267,126 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         }
         tok0 = __builtin_amdgcn_readfirstlane(tok0);
         cnt = __builtin_amdgcn_readfirstlane(cnt);
-        // Rows past the end of the cache read as zero (buffer range check) and,
-        // like rows past cnt, are masked out of the softmax.
         const uint32_t soff = (uint32_t)tok0 * (uint32_t)a.skv_t * 2u;
-        uint4 kr[C::TPL][C::CPL], vr[C::TPLV];
+        // This wave's V rows into its LDS tile (the previous unit's reads of it are
+        // complete: their results fed the previous unit's MFMAs).
 #pragma unroll
-        for (int t = 0; t < C::TPL; ++t)
+        for (int q = 0; q < NDMA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(vt + q * 1024), 16,
+                                                     (int)vof[q], (int)soff, 0, 2);
+        bf16x8_t kop[NKT][KS];
 #pragma unroll
-            for (int i = 0; i < C::CPL; ++i) kr[t][i] = buf_ld16_nt(krs, koff[t][i], soff);
+        for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int t = 0; t < C::TPLV; ++t) vr[t] = buf_ld16_nt(vrs, voff[t], soff);
+            for (int ks = 0; ks < KS; ++ks) kop[t][ks] = __builtin_bit_cast(bf16x8_t, buf_ld16_nt(krs, kof[t][ks], soff));
 
-        // Raw scores q.k of this lane group's key rows for every head.
-        float s[C::TPL][G];
+        // S^T tiles: lane (g4, n) gets head n's raw scores of tokens 16t + 4 g4 + i.
+        f32x4_t s[NKT];
 #pragma unroll
-        for (int t = 0; t < C::TPL; ++t)
+        for (int t = 0; t < NKT; ++t) {
+            s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < C::CPL; ++i) {
-                    acc = dot2_bf16(qv[h][i].x, kr[t][i].x, acc);
-                    acc = dot2_bf16(qv[h][i].y, kr[t][i].y, acc);
-                    acc = dot2_bf16(qv[h][i].z, kr[t][i].z, acc);
-                    acc = dot2_bf16(qv[h][i].w, kr[t][i].w, acc);
-                }
-                s[t][h] = group_sum<C::LPR>(acc);
-            }
+            for (int ks = 0; ks < KS; ++ks) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t][ks], qop[ks], s[t], 0, 0, 0);
+        }
         if (cnt < BS) {  // the tail unit: rows past the context take no weight
 #pragma unroll
-            for (int t = 0; t < C::TPL; ++t)
+            for (int t = 0; t < NKT; ++t)
 #pragma unroll
-                for (int h = 0; h < G; ++h) s[t][h] = wt0 + r + t * C::ROWS < cnt ? s[t][h] : -INFINITY;
+                for (int i = 0; i < 4; ++i) s[t][i] = wt0 + 16 * t + 4 * g4 + i < cnt ? s[t][i] : -INFINITY;
         }
         if constexpr (PH) {  // heads that did not keep this block give it no weight
+            if (!((hmask >> n) & 1u)) {
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-                if (!((hmask >> h) & 1u)) {
+                for (int t = 0; t < NKT; ++t) s[t] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            }
+        }
+
+        // Running max per head (log2 domain), rescale factor, weights.
+        float mx = -INFINITY;
 #pragma unroll
-                    for (int t = 0; t < C::TPL; ++t) s[t][h] = -INFINITY;
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmax_fast(mx, s[t][i]);
+        mx = max_xor32(max_xor16(mx)) * a.scale_log2;  // the head's 4 lanes; the scale is positive
+        const float m_new = fmax_fast(m_run, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_ref);
+        m_run = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[t][i] = fast_exp2(fmaf(s[t][i], a.scale_log2, -m_ref));
+                lsum += s[t][i];
+            }
+        l_part = l_part * alpha + lsum;
+        if constexpr (GT) {  // this wave's log2-sum-exp of the unit (its quarter of the tokens)
+            const float lw = sum_xor32(sum_xor16(lsum));
+            if (g4 == 0 && n < G)
+                a.blk_lse[(((int64_t)(b * a.Hkv + g) * a.units_max + u) * G + n) * C::NW + wave] =
+                    lw > 0.f ? m_ref + log2f(lw) : -INFINITY;
+        }
+        if (__ballot(alpha != 1.0f)) {  // some head's maximum moved
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        }
+
+        // P^T operands, high and low bf16 parts: k-slots 8 g4 + 4t + i <- token 16t + 4 g4 + i
+        // (k-slots 4 g4 + i for 16-token waves).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V rows are in LDS
+        if constexpr (TPW == 32) {
+            bf16x8_t ph, pl;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const __bf16 hi = (__bf16)s[t][i];
+                    ph[4 * t + i] = hi;
+                    pl[4 * t + i] = (__bf16)(s[t][i] - (float)hi);
                 }
-        }
-
-        // Wave-uniform running max per head (log2 domain), rescale factors, probabilities.
-        float alpha[G];
-        bool rescale = false;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mx = s[0][h];
-#pragma unroll
-            for (int t = 1; t < C::TPL; ++t) mx = fmax_fast(mx, s[t][h]);
-            mx = cross_group_max<C::LPR>(mx) * a.scale_log2;  // the scale is positive
-            const float m_new = fmax_fast(m_run[h], mx);
-            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-            alpha[h] = fast_exp2(m_run[h] - m_ref);
-            rescale |= alpha[h] != 1.0f;
-            m_run[h] = m_new;
-            float lsum = 0.f;
-#pragma unroll
-            for (int t = 0; t < C::TPL; ++t) {
-                s[t][h] = fast_exp2(fmaf(s[t][h], a.scale_log2, -m_ref));
-                lsum += s[t][h];
+            for (int dt = 0; dt < DT; ++dt) {
+                const char *p = vr0 + ((dt ^ tx) << 5);
+                const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+                const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)(p + 16 * D * 2));
+                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, oacc[dt], 0, 0, 0);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, oacc[dt], 0, 0, 0);
             }
-            l_part[h] = l_part[h] * alpha[h] + lsum;
-            if constexpr (GT) {  // this wave's log2-sum-exp of the unit (its quarter of the tokens)
-                const float lw = cross_group_sum<C::LPR>(lsum);
-                if (lane == 0)
-                    a.blk_lse[(((int64_t)(b * a.Hkv + g) * a.units_max + u) * G + h) * C::NW + wave] =
-                        lw > 0.f ? m_ref + log2f(lw) : -INFINITY;
+        } else {
+            v4s ph, pl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 hi = (__bf16)s[0][i];
+                ph[i] = __builtin_bit_cast(short, hi);
+                pl[i] = __builtin_bit_cast(short, (__bf16)(s[0][i] - (float)hi));
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const v4s vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)(vr0 + ((dt ^ tx) << 5)));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, ph, oacc[dt], 0, 0, 0);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pl, oacc[dt], 0, 0, 0);
             }
         }
-
-        // Probabilities to LDS (one writer per key row), then back in the PV layout.
-        if (c == 0) {
-#pragma unroll
-            for (int t = 0; t < C::TPL; ++t)
-#pragma unroll
-                for (int h = 0; h < G; ++h) p_lds[wave][r + t * C::ROWS][h] = s[t][h];
-        }
-        // LDS accesses of one wave complete in issue order; only this wave reads its slice.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        if (rescale) {  // wave-uniform: the running maxima are the same in every lane
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
-        }
-        // PV in fp32: one 16-byte value chunk per lane, every head's probability from LDS.
-#pragma unroll
-        for (int t = 0; t < C::TPLV; ++t) {
-            float p[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) p[h] = p_lds[wave][rv + t * C::ROWSV][h];
-            const uint32_t w4[4] = {vr[t].x, vr[t].y, vr[t].z, vr[t].w};
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const float v0 = bf16lo(w4[e2]), v1 = bf16hi(w4[e2]);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    o[h][2 * e2] = fmaf(p[h], v0, o[h][2 * e2]);
-                    o[h][2 * e2 + 1] = fmaf(p[h], v1, o[h][2 * e2 + 1]);
-                }
-            }
-        }
-        // The next unit overwrites p_lds; keep this unit's reads ahead of it.
-        __builtin_amdgcn_wave_barrier();
+        // The next unit's loads overwrite the tile: keep them behind this unit's reads.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Combine the wave's lane groups: sums only, the max is already wave-uniform.
+    // This wave's per-head results: the sum over the head's 4 lanes; O^T tile dt
+    // holds rows d = 16 dt + 4 g4 + i of head n.
+    const float l_tot = sum_xor32(sum_xor16(l_part));
+    if (n < G) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        l_part[h] = cross_group_sum<C::LPR>(l_part[h]);
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = cross_group_sum<C::LPV>(o[h][e]);
-    }
-    if (rv == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm_o[wave][h][cv * 8 + e] = o[h][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            sm_m[wave][h] = m_run[h];
-            sm_l[wave][h] = l_part[h];
+            for (int i = 0; i < 4; ++i) sm_o[wave][n][16 * dt + 4 * g4 + i] = oacc[dt][i];
+        if (g4 == 0) {
+            sm_m[wave][n] = m_run;
+            sm_l[wave][n] = l_tot;
         }
     }
     __syncthreads();
