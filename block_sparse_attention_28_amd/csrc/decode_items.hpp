@@ -16,17 +16,20 @@
 // every unit each wave takes a quarter of the block's tokens (32 or 16) and
 // does both products on v_mfma_f32_16x16x{32,16}_bf16 with the group's query
 // heads as the 16-wide N dimension (G <= 8 of them used):
-//   QK : S^T = K Q^T.  Each lane loads its 16-byte pieces of the K operand
-//        straight from HBM (non-temporal buffer loads; the unit's first row is
-//        a scalar offset, rows past the cache read as zero); the bf16 query
-//        is a register operand.  Lane (g4, n) gets head n's scores of tokens
-//        16t + 4 g4 + 0..3, which is exactly its slice of the P^T operand.
+//   loads : the wave's K and V rows of the unit go straight from HBM into its
+//        LDS tiles (buffer_load ... lds, non-temporal, whole 256-byte rows per
+//        16 lanes; the unit's first row is a scalar offset, rows past the
+//        cache read as zero).  A lane's 16 bytes land at base + 16 lane, so the
+//        bank-conflict swizzles below are a choice of source chunk per lane.
+//   QK : S^T = K Q^T, the K operand read from LDS (16-byte chunks XOR-swizzled
+//        by row), the bf16 query a register operand.  Lane (g4, n) gets head
+//        n's scores of tokens 16t + 4 g4 + 0..3, which is exactly its slice of
+//        the P^T operand.
 //   softmax : log2 domain, the scale folded into one FMA; one running max
 //        per head, the same in the 4 lanes of the head, accumulators rescaled
 //        only when some head's maximum moved.
-//   PV : O^T = V^T P^T.  The wave's V rows go straight into its LDS tile
-//        (buffer_load ... lds, 32-byte chunks XOR-swizzled by row) and the V^T
-//        operand is read with ds_read_b64_tr_b16.  P is split into bf16 high
+//   PV : O^T = V^T P^T, the V^T operand read from the V tile (32-byte chunks
+//        XOR-swizzled by row) with ds_read_b64_tr_b16.  P is split into bf16 high
 //        and low parts (two MFMAs), so the products keep ~16 bits of the fp32
 //        weights.
 // At the end each wave's heads and then the 4 waves are combined, and the
@@ -47,6 +50,10 @@ namespace seer {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt, lgkmcnt at max).
+constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 struct DecodeArgs {
     const uint16_t *q;
@@ -98,11 +105,12 @@ __device__ __forceinline__ void store_out(void *out, int dtype, int64_t i, float
         static_cast<uint16_t *>(out)[i] = f32_to_bf16(x);
 }
 
-// LDS of one split: each wave's V rows of the current unit, and the per-wave
-// partial results combined at the end.
+// LDS of one split: each wave's K and V rows of the current unit, and the
+// per-wave partial results combined at the end.
 template <int D, int BS, int G>
 struct DecodeSmem {
     using C = DecodeCfg<D, BS, G>;
+    __attribute__((aligned(16))) uint16_t kt[C::NW][C::TPW * D];
     __attribute__((aligned(16))) uint16_t vt[C::NW][C::TPW * D];
     float o[C::NW][G][D];
     float m[C::NW][G], l[C::NW][G];
@@ -217,21 +225,22 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, kBufferFlags);
     const int32_t *sel = (GT || PH) ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
-    uint32_t kof[NKT][KS], vof[NDMA];
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kof[t][ks] = (uint32_t)(((wt0 + 16 * t + n) * a.skv_t + 8 * g4 + 32 * ks) * 2);
-    // V tile: lane l of load q fills LDS row rr = q RPD + l / CPR, 16-byte slot s = l % CPR,
-    // with the row's 16-byte chunk whose 32-byte half-pair lands there under the swizzle.
+    // Tiles: lane l of load q fills LDS row rr = q RPD + l / CPR, 16-byte slot
+    // s = l % CPR.  K slot s holds chunk s ^ (rr & (CPR - 1)); V slot s holds
+    // the chunk whose 32-byte pair lands there when pairs are XORed with rr & XM.
+    uint32_t kof[NDMA], vof[NDMA];
 #pragma unroll
     for (int q = 0; q < NDMA; ++q) {
         const int rr = q * RPD + lane / CPR, s = lane % CPR;
-        const int c16 = ((((s >> 1) ^ (rr & XM)) << 1) | (s & 1));
-        vof[q] = (uint32_t)(((wt0 + rr) * a.skv_t + c16 * 8) * 2);
+        const int kc = s ^ (rr & (CPR - 1));
+        const int vc = ((((s >> 1) ^ (rr & XM)) << 1) | (s & 1));
+        kof[q] = (uint32_t)(((wt0 + rr) * a.skv_t + kc * 8) * 2);
+        vof[q] = (uint32_t)(((wt0 + rr) * a.skv_t + vc * 8) * 2);
     }
+    char *const kt = reinterpret_cast<char *>(sm.kt[wave]);
     char *const vt = reinterpret_cast<char *>(sm.vt[wave]);
+    // K operand reads: lane (g4, n) takes row 16t + n, chunk g4 + 4 ks.
+    const char *const kr0 = kt + n * (D * 2);
     // Transposing reads: lane (g4, s) points at tile row 16t + 4 g4 + s / 4,
     // columns 16 dt + 4 (s % 4) + 0..3; the row's swizzle does not depend on t.
     const int trow = 4 * g4 + (n >> 2), tx = trow & XM;
@@ -268,17 +277,17 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         tok0 = __builtin_amdgcn_readfirstlane(tok0);
         cnt = __builtin_amdgcn_readfirstlane(cnt);
         const uint32_t soff = (uint32_t)tok0 * (uint32_t)a.skv_t * 2u;
-        // This wave's V rows into its LDS tile (the previous unit's reads of it are
-        // complete: their results fed the previous unit's MFMAs).
+        // This wave's K and V rows into its LDS tiles (the previous unit's reads of
+        // them are complete: their results fed the previous unit's MFMAs).
+#pragma unroll
+        for (int q = 0; q < NDMA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)(kt + q * 1024), 16,
+                                                     (int)kof[q], (int)soff, 0, 2);
 #pragma unroll
         for (int q = 0; q < NDMA; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(vt + q * 1024), 16,
                                                      (int)vof[q], (int)soff, 0, 2);
-        bf16x8_t kop[NKT][KS];
-#pragma unroll
-        for (int t = 0; t < NKT; ++t)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kop[t][ks] = __builtin_bit_cast(bf16x8_t, buf_ld16_nt(krs, kof[t][ks], soff));
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(NDMA));  // the K rows are in LDS
 
         // S^T tiles: lane (g4, n) gets head n's raw scores of tokens 16t + 4 g4 + i.
         f32x4_t s[NKT];
@@ -286,7 +295,11 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         for (int t = 0; t < NKT; ++t) {
             s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t][ks], qop[ks], s[t], 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(
+                    kr0 + t * 16 * (D * 2) + (((g4 + 4 * ks) ^ (n & (CPR - 1))) << 4));
+                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ks], s[t], 0, 0, 0);
+            }
         }
         if (cnt < BS) {  // the tail unit: rows past the context take no weight
 #pragma unroll
