@@ -125,9 +125,12 @@ struct DecodeSmem {
 // PH (the per-head form): block_idx / n_sel hold one set per query head; the
 // units are the union of the group's sets, ascending, and a head gives no
 // weight to a unit it did not keep (dyn: heads_union_words(...) LDS words).
-template <int D, int BS, int G, class Mem, bool GT = false, bool PH = false>
+// KL: the kept ids and their count come from LDS (kept, kept_n) instead of
+// block_idx / n_sel.
+template <int D, int BS, int G, class Mem, bool GT = false, bool PH = false, bool KL = false>
 __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split, int g, int b,
-                                                  DecodeSmem<D, BS, G> &sm, uint32_t *dyn = nullptr) {
+                                                  DecodeSmem<D, BS, G> &sm, uint32_t *dyn = nullptr,
+                                                  const int32_t *kept = nullptr, int kept_n = 0) {
     using C = DecodeCfg<D, BS, G>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     auto &sm_o = sm.o;
@@ -191,7 +194,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         __syncthreads();
         nsel = __builtin_amdgcn_readfirstlane(sm.n_union);
     } else {
-        nsel = GT ? kcap : Mem::ldi(a.n_sel + b * a.Hkv + g);
+        nsel = GT ? kcap : (KL ? kept_n : Mem::ldi(a.n_sel + b * a.Hkv + g));
         nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
     }
     const int units = nsel + (tail > 0 ? 1 : 0);
@@ -224,7 +227,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     const uint32_t region = (uint32_t)((int64_t)a.kv_capacity * a.skv_t * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, kBufferFlags);
-    const int32_t *sel = (GT || PH) ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
+    const int32_t *sel = (GT || PH || KL) ? nullptr : a.block_idx + (int64_t)(b * a.Hkv + g) * a.k_max;
     // Tiles: lane l of load q fills LDS row rr = q RPD + l / CPR, 16-byte slot
     // s = l % CPR.  K slot s holds chunk s ^ (rr & (CPR - 1)); V slot s holds
     // the chunk whose 32-byte pair lands there when pairs are XORed with rr & XM.
@@ -263,7 +266,10 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
             } else if constexpr (!GT) {
                 if (u - id0 >= 64) {
                     id0 = u;
-                    ids = u + lane < nsel ? Mem::ldi(sel + u + lane) : 0;
+                    if constexpr (KL)
+                        ids = u + lane < nsel ? kept[u + lane] : 0;
+                    else
+                        ids = u + lane < nsel ? Mem::ldi(sel + u + lane) : 0;
                 }
                 blk = __builtin_amdgcn_readlane(ids, u - id0);
                 blk = blk < 0 ? 0 : (blk >= nc ? nc - 1 : blk);

@@ -7,10 +7,23 @@
 
 namespace seer {
 
-template <int D>
+template <int D, int QB>
 __global__ __launch_bounds__(256) void gate_scores_kernel(const GateArgs ga) {
     __shared__ GateSmem<D> sm;
-    gate_chunk_item<D, LaunchMem>(ga, blockIdx.x, blockIdx.y, sm);
+    gate_chunk_item<D, LaunchMem, QB>(ga, blockIdx.x, blockIdx.y, sm);
+}
+
+// Query rows in flight: the group size rounded up to 1, 2, 4 or 8.
+template <int D>
+static void launch_gate(const GateArgs &ga, dim3 grid, hipStream_t stream) {
+    if (ga.G == 1)
+        gate_scores_kernel<D, 1><<<grid, 256, 0, stream>>>(ga);
+    else if (ga.G == 2)
+        gate_scores_kernel<D, 2><<<grid, 256, 0, stream>>>(ga);
+    else if (ga.G <= 4)
+        gate_scores_kernel<D, 4><<<grid, 256, 0, stream>>>(ga);
+    else
+        gate_scores_kernel<D, 8><<<grid, 256, 0, stream>>>(ga);
 }
 
 }  // namespace seer
@@ -31,12 +44,9 @@ extern "C" int seer_gate_scores(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, 
     if ((int64_t)B * Hkv > 65535) return SEER_ERR_INVALID_ARG;
     if (nb_max == 0) return SEER_OK;
     GateArgs ga{q, sq_b, sq_h, wq, wk, dg, Hq / Hkv, Hkv, gate_scale, kpool, nb_max, seqlens, block_size, scores};
-    if (d == 128) {
-        dim3 grid((nb_max + GateCfg<128>::RPB - 1) / GateCfg<128>::RPB, B * Hkv);
-        gate_scores_kernel<128><<<grid, 256, 0, stream>>>(ga);
-    } else {
-        dim3 grid((nb_max + GateCfg<64>::RPB - 1) / GateCfg<64>::RPB, B * Hkv);
-        gate_scores_kernel<64><<<grid, 256, 0, stream>>>(ga);
-    }
+    if (d == 128)
+        launch_gate<128>(ga, dim3((nb_max + GateCfg<128>::RPB - 1) / GateCfg<128>::RPB, B * Hkv), stream);
+    else
+        launch_gate<64>(ga, dim3((nb_max + GateCfg<64>::RPB - 1) / GateCfg<64>::RPB, B * Hkv), stream);
     return launch_status();
 }

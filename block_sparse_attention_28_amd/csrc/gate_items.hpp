@@ -11,11 +11,11 @@
 // so each workgroup forms u = gate_scale * Wk^T (Wq qbar) for its (b, g) and
 // then streams fp32 pooled keys once: score_j = u . kp_j.
 //
-// A work item owns RPB consecutive pooled-key rows of one (b, g):
-// it issues all of their loads first (16 bytes per lane, 4 rows in flight per
-// thread and per load instruction), computes u from the L2-resident gate
-// weights while those loads are in flight, then finishes the dot products
-// with 32-lane DPP/permlane reductions.
+// A work item owns RPB consecutive pooled-key rows of one (b, g): it issues
+// the loads of the query rows and gate weights (L2-resident) and then all of
+// its pooled-key rows (16 bytes per lane, 16 rows in flight per thread), forms
+// u while the pooled rows arrive, then finishes the dot products with 32-lane
+// DPP/permlane reductions.
 #pragma once
 
 #include "seer_device.hpp"
@@ -57,10 +57,13 @@ struct GateSmem {
     float u[D];
 };
 
-// Rows [chunk * RPB, (chunk + 1) * RPB) of the scores of pair = b * Hkv + g.
-// Every thread of the 256-thread workgroup calls it.
-template <int D, class Mem>
-__device__ __forceinline__ void gate_chunk_item(const GateArgs &ga, int chunk, int pair, GateSmem<D> &sm) {
+// Rows [jb, je) of the scores of pair = b * Hkv + g (je <= nb_max): u . kp_j
+// for the complete blocks among them, -inf for the rest.  Every thread of the
+// 256-thread workgroup calls it.  QB: query rows loaded up front (at least
+// min(G, 8) keeps every row of a group of up to 8 in flight with the weights;
+// rows past QB are loaded when used).
+template <int D, class Mem, int QB = 8>
+__device__ __forceinline__ void gate_rows_item(const GateArgs &ga, int pair, int jb, int je, GateSmem<D> &sm) {
     const uint16_t *q = ga.q;
     const int64_t sq_b = ga.sq_b, sq_h = ga.sq_h;
     const uint16_t *wq = ga.wq, *wk = ga.wk;
@@ -80,59 +83,73 @@ __device__ __forceinline__ void gate_chunk_item(const GateArgs &ga, int chunk, i
     L = L < 0 ? 0 : L;
     int nc = L / block_size;
     nc = nc > nb_max ? nb_max : nc;
-    const int j0 = chunk * C::RPB;
+    const int jv = je < nc ? je : nc;  // rows [jb, jv) are complete blocks
     float *srow = scores + (int64_t)pair * nb_max;
-    if (j0 >= nc) {  // nothing complete here: only -inf to write
-        for (int j = j0 + tid; j < j0 + C::RPB && j < nb_max; j += 256) Mem::stf(srow + j, -INFINITY);
-        return;
-    }
+    for (int j = (jb > jv ? jb : jv) + tid; j < je; j += 256) Mem::stf(srow + j, -INFINITY);
+    if (jb >= jv) return;  // nothing complete here
 
-    // 1. Pooled-key rows of this workgroup, all loads issued up front.
-    const float *kp = kpool + (int64_t)pair * nb_max * D;
+    // 1. Loads in the order they are used: the group's query rows and the first
+    // Wq and Wk rows (L2-resident), then this item's pooled-key rows.  A barrier
+    // between the two puts every wave's weight requests ahead of the pooled-key
+    // stream, so u is formed while the pooled rows are still arriving.  All go
+    // through buffer descriptors whose ranges end at the last valid row: rows
+    // past it (heads >= G, weight rows >= dg, blocks >= nc) read as zero, so no
+    // branch separates the loads and all of them stay in flight together.
+    const int c = tid % C::CH, rg = tid / C::CH;
+    constexpr int WB = 8;  // weight rows per thread in flight
+    const uint16_t *qg = q + b * sq_b + (int64_t)(g * G) * sq_h;
+    const auto qrs = buffer_rsrc(qg, (uint32_t)(((int64_t)(G - 1) * sq_h + D) * 2));
+    const auto wqrs = buffer_rsrc(wq + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
+    const auto wkrs = buffer_rsrc(wk + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
+    auto wrow = [&](int r) { return (uint32_t)(r * D * 2 + c * 16); };
+    uint4 qw[QB], wqv[WB], wkv[WB];
+#pragma unroll
+    for (int h = 0; h < QB; ++h) qw[h] = buf_ld16(qrs, (uint32_t)(h * sq_h * 2) + c * 16, 0);
+#pragma unroll
+    for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(rg + i * C::RG), 0);
+#pragma unroll
+    for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)jv * D * 4);
     float4 x[C::ITER];
 #pragma unroll
-    for (int it = 0; it < C::ITER; ++it) {
-        const int j = j0 + lr + it * C::ROWS;
-        x[it] = j < nc ? reinterpret_cast<const float4 *>(kp + (int64_t)j * D)[lc] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int it = 0; it < C::ITER; ++it)
+        x[it] = as_float4(buf_ld16_nt(kprs, (uint32_t)((jb + lr + it * C::ROWS) * D * 4 + lc * 16), 0));
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. u = gate_scale * Wk^T (Wq qbar) for (b, g).
-    const int c = tid % C::CH, rg = tid / C::CH;
-    // Each thread owns the 16-byte column chunk c of weight rows rg, rg + RG, ...,
-    // taken 8 rows at a time with all 8 loads issued before any is used.
-    constexpr int WB = 8;
-    const uint16_t *qg = q + b * sq_b + (int64_t)(g * G) * sq_h + c * 8;
+    // 2. u = gate_scale * Wk^T (Wq qbar) for (b, g).  Thread (c, rg) owns the
+    // 16-byte column chunk c of weight rows rg, rg + RG, ..., WB rows at a time.
     float qb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int h0 = 0; h0 < G; h0 += 4) {
-        uint4 qw[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-            qw[h] = h0 + h < G ? *reinterpret_cast<const uint4 *>(qg + (h0 + h) * sq_h) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < QB; ++h) {
+        if (h < G) {
             float f[8];
             unpack8(qw[h], f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) qb[e] += f[e];
         }
     }
+    for (int h = QB; h < G; ++h) {  // groups wider than QB heads
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4 *>(qg + h * sq_h + c * 8), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[e] += f[e];
+    }
     const float inv_g = 1.0f / (float)G;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qb[e] *= inv_g;
-    const uint16_t *wqg = wq + (int64_t)g * dg * D + c * 8;
-    const uint16_t *wkg = wk + (int64_t)g * dg * D + c * 8;
     for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {  // a[r] = Wq[r] . qbar
-        uint4 w[WB];
+        if (r0 > 0) {
 #pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            const int r = r0 + rg + i * C::RG;
-            w[i] = r < dg ? *reinterpret_cast<const uint4 *>(wqg + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(r0 + rg + i * C::RG), 0);
         }
 #pragma unroll
         for (int i = 0; i < WB; ++i) {
             const int r = r0 + rg + i * C::RG;
             float f[8];
-            unpack8(w[i], f);
+            unpack8(wqv[i], f);
             float s = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) s = fmaf(f[e], qb[e], s);
@@ -143,17 +160,15 @@ __device__ __forceinline__ void gate_chunk_item(const GateArgs &ga, int chunk, i
     __syncthreads();
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {  // u += a[r] * Wk[r]
-        uint4 w[WB];
+        if (r0 > 0) {
 #pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            const int r = r0 + rg + i * C::RG;
-            w[i] = r < dg ? *reinterpret_cast<const uint4 *>(wkg + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(r0 + rg + i * C::RG), 0);
         }
 #pragma unroll
         for (int i = 0; i < WB; ++i) {
             const int r = r0 + rg + i * C::RG;
             float f[8];
-            unpack8(w[i], f);
+            unpack8(wkv[i], f);
             const float ar = r < dg ? a_s[r] : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = fmaf(ar, f[e], acc[e]);
@@ -170,19 +185,33 @@ __device__ __forceinline__ void gate_chunk_item(const GateArgs &ga, int chunk, i
     }
     __syncthreads();
 
-    // 3. score_j = u . kp_j
+    // 3. score_j = u . kp_j, RPB rows at a time.
     const float4 uu = reinterpret_cast<const float4 *>(u_s)[lc];
+    for (int j0 = jb;;) {
 #pragma unroll
-    for (int it = 0; it < C::ITER; ++it) {
-        const int j = j0 + lr + it * C::ROWS;
-        float s = uu.x * x[it].x;
-        s = fmaf(uu.y, x[it].y, s);
-        s = fmaf(uu.z, x[it].z, s);
-        s = fmaf(uu.w, x[it].w, s);
-        s = group_sum<16>(s);
-        if constexpr (C::LPR == 32) s = sum_xor16(s);
-        if (lc == 0 && j < nb_max) Mem::stf(srow + j, j < nc ? s : -INFINITY);
+        for (int it = 0; it < C::ITER; ++it) {
+            const int j = j0 + lr + it * C::ROWS;
+            float s = uu.x * x[it].x;
+            s = fmaf(uu.y, x[it].y, s);
+            s = fmaf(uu.z, x[it].z, s);
+            s = fmaf(uu.w, x[it].w, s);
+            s = group_sum<16>(s);
+            if constexpr (C::LPR == 32) s = sum_xor16(s);
+            if (lc == 0 && j < jv) Mem::stf(srow + j, s);
+        }
+        j0 += C::RPB;
+        if (j0 >= jv) break;
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it)
+            x[it] = as_float4(buf_ld16_nt(kprs, (uint32_t)((j0 + lr + it * C::ROWS) * D * 4 + lc * 16), 0));
     }
+}
+
+// Rows [chunk * RPB, (chunk + 1) * RPB) of the scores of pair = b * Hkv + g.
+template <int D, class Mem, int QB = 8>
+__device__ __forceinline__ void gate_chunk_item(const GateArgs &ga, int chunk, int pair, GateSmem<D> &sm) {
+    const int jb = chunk * GateCfg<D>::RPB, je = jb + GateCfg<D>::RPB;
+    gate_rows_item<D, Mem, QB>(ga, pair, jb, je < ga.nb_max ? je : ga.nb_max, sm);
 }
 
 }  // namespace seer

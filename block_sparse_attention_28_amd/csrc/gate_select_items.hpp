@@ -11,13 +11,11 @@
 //     pooled-key rows are still arriving.
 //  2. score_j = u . kp_j for the complete blocks, written to the scores output
 //     and, as order-preserving keys, to LDS.
-//  3. A block-wide 8-bit radix select over the LDS keys finds the k-th largest
-//     key T and how many keys equal to T to take (the lower ids among equal
-//     keys); one sweep in id order then places each kept id with ballot counts
-//     per wave, so block_idx comes out ascending.
+//  3. The block-wide selection of topk_block.hpp over those LDS keys.
 #pragma once
 
 #include "gate_items.hpp"
+#include "topk_block.hpp"
 #include "topk_wave.hpp"
 
 namespace seer {
@@ -70,9 +68,7 @@ struct GsSmem {
     float a[256];                   // Wq qbar
     float u_part[GsCfg<D, NT>::NW][D];
     float u[D];
-    int hist[3][256];                 // radix histograms, used in rotation
-    float red[2][GsCfg<D, NT>::NW];   // threshold policy: per-wave max and sum
-    int wcnt[2][2][GsCfg<D, NT>::NW];  // per-wave counts of the id sweep, double-buffered
+    SelBlockSmem<NT> sel;
 };
 
 struct GateSelectArgs {
@@ -157,7 +153,7 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
             if (c == 0 && r < dg) sm.a[r] = s;
         }
     }
-    if (tid < 256) sm.hist[0][tid] = 0;  // first radix histogram, ordered by the barriers below
+    block_select_prepare<NT>(sm.sel);  // ordered before the selection by the barriers below
     __syncthreads();
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -225,114 +221,8 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
     __syncthreads();  // keys complete
 
     // 4. Selection: k blocks by the policy, ids ascending, -1 after.
-    const int k_max = gs.k_max;
-    int k = policy_count(gs.pol, nc, k_max);
-    if (gs.pol.kind == 2 && k > 0) {  // threshold: count the blocks with probability >= tau
-        float m = -INFINITY;
-        for (int j = tid; j < nc; j += NT) m = fmax_fast(m, key_to_float(keys[j]));
-        m = wave_max(m);
-        if (lane == 0) sm.red[0][wave] = m;
-        __syncthreads();
-        m = sm.red[0][0];
-#pragma unroll
-        for (int w = 1; w < C::NW; ++w) m = fmax_fast(m, sm.red[0][w]);
-        float z = 0.f;
-        for (int j = tid; j < nc; j += NT) z += expf(key_to_float(keys[j]) - m);
-        z = wave_sum(z);
-        if (lane == 0) sm.red[1][wave] = z;
-        __syncthreads();
-        z = 0.f;
-#pragma unroll
-        for (int w = 0; w < C::NW; ++w) z += sm.red[1][w];
-        const float bar = gs.pol.tau * z;
-        float cnt = 0.f;
-        for (int j = tid; j < nc; j += NT) cnt += expf(key_to_float(keys[j]) - m) >= bar ? 1.f : 0.f;
-        cnt = wave_sum(cnt);
-        __syncthreads();  // every wave has read red[0]
-        if (lane == 0) sm.red[0][wave] = cnt;
-        __syncthreads();
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < C::NW; ++w) c += (int)sm.red[0][w];
-        c = __builtin_amdgcn_readfirstlane(c);
-        k = c < k ? c : k;
-    }
-    int32_t *out = gs.block_idx + (int64_t)pair * k_max;
-    if (k == nc || k == 0) {  // every complete block, or none, is kept
-        for (int i = tid; i < k_max; i += NT) Mem::sti(out + i, i < k ? i : -1);
-    } else {
-        // Radix passes over 8-bit digits from the top.  Every wave scans the
-        // histogram itself (one barrier per pass); histograms rotate over three
-        // buffers so the one zeroed during a pass was last read two passes ago.
-        uint32_t prefix = 0;
-        int need = k;
-#pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-            int *hist = sm.hist[pass % 3];
-            if (tid < 256) sm.hist[(pass + 1) % 3][tid] = 0;
-            for (int j = tid; j < nc; j += NT) {
-                const uint32_t key = keys[j];
-                if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-            }
-            __syncthreads();
-            // lane l covers digits 255-4l .. 252-4l, in descending order
-            int cnt[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - 4 * lane - i];
-            const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-            const int incl = wave_inclusive_scan(local, lane);
-            const int excl = incl - local;
-            int digit = 0, rest = 0;
-            {
-                int cum = excl;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (cum < need && cum + cnt[i] >= need) {  // the one digit where the count crosses need
-                        digit = 255 - 4 * lane - i;
-                        rest = need - cum;
-                    }
-                    cum += cnt[i];
-                }
-            }
-            const uint64_t hit = __ballot(excl < need && incl >= need);  // exactly one lane
-            const int src = hit ? (int)__builtin_ctzll(hit) : 0;
-            prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, src) << shift;
-            need = __builtin_amdgcn_readlane(rest, src);
-        }
-        // Keep keys > T and the first `need` keys == T in id order; the position of a
-        // kept id is the number of kept ids below it.
-        const uint32_t T = prefix;
-        int gt_seen = 0, eq_seen = 0;
-        for (int base = 0, round = 0; base < nc; base += NT, round ^= 1) {
-            const int j = base + tid;
-            const uint32_t key = j < nc ? keys[j] : 0u;
-            const bool gt = j < nc && key > T, eq = j < nc && key == T;
-            const uint64_t gt_mask = __ballot(gt), eq_mask = __ballot(eq);
-            if (lane == 0) {
-                sm.wcnt[round][0][wave] = __popcll(gt_mask);
-                sm.wcnt[round][1][wave] = __popcll(eq_mask);
-            }
-            __syncthreads();
-            int gt_below = gt_seen + lanes_below(gt_mask), eq_below = eq_seen + lanes_below(eq_mask);
-            int gt_all = gt_seen, eq_all = eq_seen;
-#pragma unroll
-            for (int w = 0; w < C::NW; ++w) {
-                const int cg = sm.wcnt[round][0][w], ce = sm.wcnt[round][1][w];
-                if (w < wave) {
-                    gt_below += cg;
-                    eq_below += ce;
-                }
-                gt_all += cg;
-                eq_all += ce;
-            }
-            if (gt || (eq && eq_below < need)) Mem::sti(out + gt_below + (eq_below < need ? eq_below : need), j);
-            gt_seen = gt_all;
-            eq_seen = eq_all;
-        }
-        for (int i = k + tid; i < k_max; i += NT) Mem::sti(out + i, -1);
-    }
+    const int k = block_select_keys<NT, Mem>(keys, nc, gs.pol, gs.k_max, gs.block_idx + (int64_t)pair * gs.k_max,
+                                             nullptr, sm.sel);
     if (tid == 0) Mem::sti(gs.n_sel + pair, k);
 }
 

@@ -7,29 +7,48 @@
 // id, and emit the kept ids in ascending order (so decoding reads memory
 // forward).
 //
-// One wavefront per (b, head), several per workgroup, no workgroup barriers;
-// the exact radix top-k itself is in topk_wave.hpp.
+// One 256-thread workgroup per (b, head): the scores go to LDS as
+// order-preserving keys and the block-wide selection of topk_block.hpp picks
+// from them (the rule itself is stated in topk_wave.hpp).
 #include "seer_device.hpp"
 #include "seer_host.hpp"
-#include "topk_wave.hpp"
+#include "topk_block.hpp"
 
 namespace seer {
 
-constexpr int kSelMaxBlocks = 16384 - 256;  // keys + histogram of one wave fit in 64 KiB of LDS
+constexpr int kSelThreads = 256;
+constexpr int kSelMaxBlocks = 16384 - 256;  // LDS keys of one pair (64 KiB less a histogram's worth)
 
-__global__ __launch_bounds__(256) void select_blocks_kernel(const float *scores, const int32_t *seqlens, int B,
-                                                            int H, int nb_max, int slice, int block_size, int k_max,
-                                                            int32_t *block_idx, int32_t *n_sel,
-                                                            const SelectPolicy pol) {
-    extern __shared__ uint32_t lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int pair = blockIdx.x * (blockDim.x >> 6) + wave;  // b * H + h
-    if (pair >= B * H) return;
-    uint32_t *keys = lds + (size_t)wave * slice;              // [nb_max]
-    int *hist = reinterpret_cast<int *>(keys + slice - 256);  // [256]
-
-    select_pair_item<LaunchMem>(scores, seqlens, H, nb_max, block_size, k_max, block_idx, n_sel, pair, keys, hist,
-                                lane, pol);
+__global__ __launch_bounds__(kSelThreads) void select_blocks_kernel(const float *scores, const int32_t *seqlens,
+                                                                    int H, int nb_max, int block_size, int k_max,
+                                                                    int32_t *block_idx, int32_t *n_sel,
+                                                                    const SelectPolicy pol) {
+    extern __shared__ uint32_t keys[];  // [nb_max]
+    __shared__ SelBlockSmem<kSelThreads> sm;
+    const int pair = blockIdx.x;  // b * H + h
+    int L = seqlens[pair / H];
+    L = L < 0 ? 0 : L;
+    int nc = L / block_size;
+    nc = nc > nb_max ? nb_max : nc;
+    nc = __builtin_amdgcn_readfirstlane(nc);
+    // Four loads per thread in flight; rows past nc read as zero.
+    const auto rs = buffer_rsrc(scores + (int64_t)pair * nb_max, (uint32_t)nc * 4);
+    for (int j0 = 0; j0 < nc; j0 += 4 * kSelThreads) {
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (j0 + i * kSelThreads + (int)threadIdx.x) * 4, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + i * kSelThreads + (int)threadIdx.x;
+            if (j < nc) keys[j] = order_key(__uint_as_float(v[i]));
+        }
+    }
+    block_select_prepare<kSelThreads>(sm);
+    __syncthreads();  // keys complete
+    const int k = block_select_keys<kSelThreads, LaunchMem>(keys, nc, pol, k_max, block_idx + (int64_t)pair * k_max,
+                                                            nullptr, sm);
+    if (threadIdx.x == 0) n_sel[pair] = k;
 }
 
 // Host-side check of a selection policy; NULL means the token budget.
@@ -60,15 +79,10 @@ extern "C" int seer_select_blocks_ex(const float *scores, const int32_t *seqlens
     if ((k_max > 0 && !block_idx) || (nb_max > 0 && !scores)) return SEER_ERR_INVALID_ARG;
     if (nb_max > kSelMaxBlocks) return SEER_ERR_UNSUPPORTED;
     const int64_t pairs = (int64_t)B * H;
-    if (pairs > (1LL << 30)) return SEER_ERR_INVALID_ARG;
-    // LDS slice per wave: the keys plus a 256-bin histogram; up to 4 waves while it stays within 64 KiB.
-    const int slice = nb_max + 256;
-    int waves = (int)(65536 / ((size_t)slice * 4));
-    waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
-    const size_t shmem = (size_t)waves * slice * sizeof(uint32_t);
-    const int grid = (int)((pairs + waves - 1) / waves);
-    select_blocks_kernel<<<dim3(grid), 64 * waves, shmem, stream>>>(scores, seqlens, B, H, nb_max, slice,
-                                                                    block_size, k_max, block_idx, n_sel, pol);
+    if (pairs > 0x7fffffffLL) return SEER_ERR_INVALID_ARG;
+    const size_t shmem = (size_t)nb_max * sizeof(uint32_t);
+    select_blocks_kernel<<<dim3((unsigned)pairs), kSelThreads, shmem, stream>>>(scores, seqlens, H, nb_max, block_size,
+                                                                               k_max, block_idx, n_sel, pol);
     return launch_status();
 }
 

@@ -2,27 +2,29 @@
 //
 // The same work as seer_gate_scores + seer_select_blocks + seer_sparse_decode
 // (gate chunks, per-(b, KV head) selection, decode splits, log-sum-exp merges;
-// see gate_items.hpp, topk_wave.hpp and decode_items.hpp for the operation),
+// see gate_items.hpp, topk_block.hpp and decode_items.hpp for the operation),
 // but run by one grid of resident workgroups: workgroup w takes work items
-// w, w + grid, w + 2 grid, ... in increasing order.  Items are numbered in
-// dependency order -- all gate chunks, then the selections (one per pair),
-// then the decode splits pair by pair, then the merges -- so an item only ever
-// waits for items with smaller numbers: the smallest unfinished item always has
-// its inputs ready, hence no deadlock while the whole grid is resident (the
-// grid is sized from the occupancy of this kernel), and a pair's selection or
-// decode starts as soon as its own inputs are ready instead of after a kernel
-// boundary.
+// w, w + grid, w + 2 grid, ... in increasing order.  Item (pair, split) for
+// split < S does all of that split's work: its share of the pair's gate rows
+// (the complete blocks dealt evenly over the S splits), then -- once the
+// pair's S shares are in -- the pair's selection, which every split computes
+// itself in LDS (it is exact and deterministic, so the S splits agree; split 0
+// also writes it out), then the split's decode; the pair's last split to
+// finish merges the S partial results.  The grid is a multiple of S, so the S
+// items of a pair always run in the same round, on workgroups that are
+// resident together (the grid is sized from the occupancy of this kernel), and
+// no other wait exists: no deadlock, and every workgroup has the same work.
 //
-// Hand-offs between workgroups (scores, kept ids and counts, split partials)
-// use device-coherent loads and stores (the workgroups may sit on different
-// XCDs with separate L2s); a producer waits for its stores to complete before
-// bumping the item's counter, a consumer polls that counter.  Every poll loop
-// has a limit and a shared abort word, so a launch always terminates; the last
-// workgroup out clears the counters for the next launch.
+// Hand-offs between workgroups (scores, split partials) use device-coherent
+// loads and stores (the workgroups may sit on different XCDs with separate
+// L2s); a producer waits for its stores to complete before bumping the item's
+// counter, a consumer polls that counter.  Every poll loop has a limit and a
+// shared abort word, so a launch always terminates; the last workgroup out
+// clears the counters for the next launch.
 #include "decode_items.hpp"
 #include "gate_items.hpp"
 #include "seer_host.hpp"
-#include "topk_wave.hpp"
+#include "topk_block.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -36,10 +38,9 @@ struct StepArgs {
     GateArgs gate;
     DecodeArgs dec;
     int pairs;        // B * Hkv
-    int chunks;       // gate chunks per pair
     int k_max;
-    int *ctl;         // [kCtlWords + 3 * pairs]
-    int n_gate, n_select, n_decode, total;
+    int *ctl;         // [kCtlWords + 2 * pairs]
+    int total;            // pairs * S items
 };
 
 __device__ __forceinline__ int ld_dev(int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -62,6 +63,35 @@ __device__ __forceinline__ void wait_for(int *ctr, int target, int *status) {
     __syncthreads();
 }
 
+// The scores [0, nc) of a pair as selection keys in LDS: device-coherent (sc1)
+// buffer loads, four per thread in flight; rows past nc read as zero.
+constexpr int kCoherentLoad = 16;  // cache policy: sc1
+__device__ __forceinline__ void load_keys(const float *row, int nc, uint32_t *keys) {
+    const auto rs = buffer_rsrc(row, (uint32_t)nc * 4);
+    for (int j0 = 0; j0 < nc; j0 += 4 * 256) {
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (j0 + i * 256 + (int)threadIdx.x) * 4, 0, kCoherentLoad);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + i * 256 + (int)threadIdx.x;
+            if (j < nc) keys[j] = order_key(__uint_as_float(v[i]));
+        }
+    }
+}
+
+// As signal_done; true, in every thread, for the workgroup whose increment
+// brought the counter to `target` (every other producer's stores are then
+// complete and visible).
+__device__ __forceinline__ bool signal_done_last(int *ctr, int target, int *s_old) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) *s_old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_old) == target - 1;
+}
+
 // Every thread's device-coherent stores of this item have completed; then one increment.
 __device__ __forceinline__ void signal_done(int *ctr) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -74,41 +104,46 @@ union StepSmem {
     DecodeSmem<D, BS, G> dec;
     GateSmem<D> gate;
     MergeSmem merge;
+    SelBlockSmem<256> sel;
 };
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(256, 2) void decode_step_kernel(const StepArgs s) {
     __shared__ StepSmem<D, BS, G> sm;
-    extern __shared__ uint32_t sel_lds[];  // selection keys [nb_max] + histogram [256], used by wave 0
+    extern __shared__ uint32_t keys[];  // selection keys [nb_max], then the kept ids in place
     int *ctl = s.ctl;
-    int *gate_done = ctl + kCtlWords, *sel_done = gate_done + s.pairs, *dec_done = sel_done + s.pairs;
+    int *gate_done = ctl + kCtlWords, *dec_done = gate_done + s.pairs;
     int *status = ctl + kCtlStatus;
-    const int S = s.dec.num_splits, Hkv = s.dec.Hkv;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = s.dec.num_splits, Hkv = s.dec.Hkv, nb_max = s.gate.nb_max;
+    __shared__ int s_flag;
     for (int item = blockIdx.x; item < s.total; item += gridDim.x) {
         __syncthreads();  // the previous item's LDS use is over
-        if (item < s.n_gate) {
-            const int pair = item / s.chunks, chunk = item % s.chunks;
-            gate_chunk_item<D, DeviceMem>(s.gate, chunk, pair, sm.gate);
-            signal_done(gate_done + pair);
-        } else if (item < s.n_gate + s.n_select) {
-            const int pair = item - s.n_gate;
-            wait_for(gate_done + pair, s.chunks, status);
-            if (wave == 0)
-                select_pair_item<DeviceMem>(s.gate.scores, s.gate.seqlens, Hkv, s.gate.nb_max, s.gate.block_size,
-                                            s.k_max, const_cast<int32_t *>(s.dec.block_idx),
-                                            const_cast<int32_t *>(s.dec.n_sel), pair, sel_lds,
-                                            reinterpret_cast<int *>(sel_lds + s.gate.nb_max), threadIdx.x);
-            signal_done(sel_done + pair);
-        } else if (item < s.n_gate + s.n_select + s.n_decode) {
-            const int idx = item - s.n_gate - s.n_select, pair = idx / S, split = idx % S;
-            wait_for(sel_done + pair, 1, status);
-            decode_split_item<D, BS, G, DeviceMem>(s.dec, split, pair % Hkv, pair / Hkv, sm.dec);
-            if (S > 1) signal_done(dec_done + pair);
-        } else {
-            const int pair = item - s.n_gate - s.n_select - s.n_decode;
-            wait_for(dec_done + pair, S, status);
-            const int b = pair / Hkv, g = pair % Hkv;
+        const int pair = item / S, split = item % S;
+        const int b = pair / Hkv, g = pair % Hkv;
+        int L = s.gate.seqlens[b];
+        L = L < 0 ? 0 : L;
+        int nc = L / s.gate.block_size;
+        nc = nc > nb_max ? nb_max : nc;
+        nc = __builtin_amdgcn_readfirstlane(nc);
+        // This split's gate rows; the last split also writes -inf past the complete blocks.
+        const int jb = (int)((int64_t)split * nc / S);
+        const int je = split == S - 1 ? nb_max : (int)((int64_t)(split + 1) * nc / S);
+        gate_rows_item<D, DeviceMem, G>(s.gate, pair, jb, je, sm.gate);
+        signal_done(gate_done + pair);
+        wait_for(gate_done + pair, S, status);
+        // The pair's selection, from its complete scores.
+        load_keys(s.gate.scores + (int64_t)pair * nb_max, nc, keys);
+        block_select_prepare<256>(sm.sel);
+        __syncthreads();  // keys complete
+        int32_t *kept = reinterpret_cast<int32_t *>(keys);
+        int32_t *out = split == 0 ? const_cast<int32_t *>(s.dec.block_idx) + (int64_t)pair * s.k_max : nullptr;
+        const int k = block_select_keys<256, DeviceMem>(keys, nc, SelectPolicy{0, 1, 1, 0.f}, s.k_max, out,
+                                                        kept, sm.sel);
+        if (split == 0 && threadIdx.x == 0) DeviceMem::sti(const_cast<int32_t *>(s.dec.n_sel) + pair, k);
+        __syncthreads();  // kept ids complete; the selection's LDS is free for the decode tiles
+        decode_split_item<D, BS, G, DeviceMem, false, false, true>(s.dec, split, g, b, sm.dec, nullptr, kept, k);
+        // The pair's last split to finish merges the S partial results.
+        if (S > 1 && signal_done_last(dec_done + pair, S, &s_flag)) {
             for (int h = 0; h < G; ++h)
                 decode_merge_row<D, DeviceMem>(s.dec.part_o, s.dec.part_ml, S, (int64_t)b * s.dec.Hq + g * G + h,
                                                s.dec.out, s.dec.out_dtype, s.dec.lse, sm.merge);
@@ -122,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(const StepArgs s) {
                  (int)gridDim.x - 1;
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(s_last)) {
-        for (int i = threadIdx.x; i < 3 * s.pairs; i += blockDim.x)
+        for (int i = threadIdx.x; i < 2 * s.pairs; i += blockDim.x)
             __hip_atomic_store(gate_done + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (threadIdx.x == 0) __hip_atomic_store(ctl + kCtlFinished, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -134,9 +169,12 @@ static int launch_step(const StepArgs &s, size_t sel_lds_bytes, hipStream_t stre
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, sel_lds_bytes) != hipSuccess || per_cu < 1)
         per_cu = 1;
+    // A multiple of S (a pair's S items share a round) that is at least S.
+    const int S = s.dec.num_splits;
     int grid = device_cu_count() * per_cu;
     grid = grid < s.total ? grid : s.total;
-    grid = grid < 1 ? 1 : grid;
+    grid = grid / S * S;
+    grid = grid < S ? S : grid;
     kernel<<<dim3(grid), 256, sel_lds_bytes, stream>>>(s);
     return launch_status();
 }
@@ -152,7 +190,7 @@ static int step_dispatch_group(const StepArgs &s, size_t lds, int G, hipStream_t
     return SEER_ERR_UNSUPPORTED;
 }
 
-static size_t step_ctl_bytes(int pairs) { return ((size_t)(kCtlWords + 3 * pairs) * sizeof(int) + 255) / 256 * 256; }
+static size_t step_ctl_bytes(int pairs) { return ((size_t)(kCtlWords + 2 * pairs) * sizeof(int) + 255) / 256 * 256; }
 
 }  // namespace seer
 
@@ -195,7 +233,6 @@ extern "C" int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, 
         return SEER_ERR_WORKSPACE;
 
     StepArgs s;
-    const int rpb = d == 128 ? GateCfg<128>::RPB : GateCfg<64>::RPB;
     s.gate = GateArgs{q, sq_b, sq_h, wq, wk, dg, G, Hkv, gate_scale, kpool, nb_max, seqlens, block_size, scores};
     char *ws = static_cast<char *>(workspace);
     DecodeArgs &a = s.dec;
@@ -210,14 +247,10 @@ extern "C" int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, 
     a.out = out; a.out_dtype = out_dtype; a.lse = lse;
     a.blk_lse = nullptr; a.units_max = 0;
     s.pairs = pairs;
-    s.chunks = (nb_max + rpb - 1) / rpb;
     s.k_max = k_max;
     s.ctl = reinterpret_cast<int *>(ws);
-    s.n_gate = pairs * s.chunks;
-    s.n_select = pairs;
-    s.n_decode = pairs * S;
-    s.total = s.n_gate + s.n_select + s.n_decode + (S > 1 ? pairs : 0);
-    const size_t lds = ((size_t)nb_max + 256) * sizeof(uint32_t);
+    s.total = pairs * S;
+    const size_t lds = (size_t)nb_max * sizeof(uint32_t);
     if (d == 128)
         return block_size == 128 ? step_dispatch_group<128, 128>(s, lds, G, stream)
                                  : step_dispatch_group<128, 64>(s, lds, G, stream);

@@ -271,9 +271,10 @@ int seer_decode_block_mass(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
  * One whole decode step in a single launch: the gate scores, the token-budget
  * selection and the sparse decode with its merge -- the same results, bit for
  * bit, as seer_gate_scores + seer_select_blocks + seer_sparse_decode with the
- * same arguments, but run by one persistent grid whose workgroups pick up
- * each (b, KV head)'s selection and decode as soon as that pair's inputs are
- * ready (no kernel boundaries in between).
+ * same arguments, but run by one persistent grid: each decode split of a
+ * (b, KV head) starts as soon as that pair's gate scores are complete, selects
+ * the pair's blocks itself in LDS and decodes (no kernel boundaries in
+ * between).
  *   arguments as in the three calls above; scores [B][Hkv][nb_max],
  *   block_idx [B][Hkv][budget_tokens / block_size] and n_sel [B][Hkv] are
  *   written as those calls write them.
