@@ -22,14 +22,14 @@
 
 namespace seer {
 
-template <int D>
+template <int D, int NT = 256>
 struct GateCfg {
     static constexpr int LPR = D / 4;        // lanes per pooled-key row (4 floats each)
-    static constexpr int ROWS = 256 / LPR;   // rows per workgroup-wide load: 8 or 16
-    static constexpr int ITER = 16;          // row loads in flight per thread
-    static constexpr int RPB = ROWS * ITER;  // rows per workgroup
+    static constexpr int ROWS = NT / LPR;    // rows per workgroup-wide load
+    static constexpr int ITER = NT >= 1024 ? 8 : 16;  // row loads in flight per thread
+    static constexpr int RPB = ROWS * ITER;  // rows per batch: 128 (d 128) at 256 threads, 256 at 1024
     static constexpr int CH = D / 8;         // 16-byte bf16 chunks per weight row: 16 or 8
-    static constexpr int RG = 256 / CH;      // weight-row groups: 16 or 32
+    static constexpr int RG = 256 / CH;      // weight-row groups of the first 256 threads: 16 or 32
 };
 
 __device__ __forceinline__ void unpack8(const uint4 w, float *f) {
@@ -57,136 +57,158 @@ struct GateSmem {
     float u[D];
 };
 
+// The gate vector u = gate_scale * Wk^T (Wq qbar) of (b, g), formed by the
+// first 256 threads of the workgroup: thread t owns the 16-byte column chunk
+// t % CH of weight rows t / CH + RG i.  issue() starts the loads of the query
+// rows and of the first Wq and Wk rows (threads >= 256 issue nothing), through
+// buffer descriptors whose ranges end at the last valid row, so heads >= G and
+// weight rows >= dg read as zero and no branch separates the loads.  finish()
+// leaves u in sm.u; every thread of the workgroup calls it (it holds barriers).
+// Workgroups of any size >= 256 therefore form u in the same order, bit for bit.
+// LATE_WK: load the Wk rows only once a is formed (fewer registers held while
+// the pooled rows are in flight, one more L2 round trip on u's path).
+template <int D, int QB, bool LATE_WK = false>
+struct GateU {
+    using C = GateCfg<D>;
+    static constexpr int WB = 8;  // weight rows per thread in flight
+    uint4 qw[QB], wqv[WB], wkv[WB];
+
+    __device__ __forceinline__ void issue(const GateArgs &ga, int b, int g) {
+        const int tid = threadIdx.x, c = tid % C::CH, rg = tid / C::CH;
+        if (tid >= 256) return;
+        const uint16_t *qg = ga.q + b * ga.sq_b + (int64_t)(g * ga.G) * ga.sq_h;
+        const auto qrs = buffer_rsrc(qg, (uint32_t)(((int64_t)(ga.G - 1) * ga.sq_h + D) * 2));
+        const auto wqrs = buffer_rsrc(ga.wq + (int64_t)g * ga.dg * D, (uint32_t)(ga.dg * D * 2));
+        const auto wkrs = buffer_rsrc(ga.wk + (int64_t)g * ga.dg * D, (uint32_t)(ga.dg * D * 2));
+#pragma unroll
+        for (int h = 0; h < QB; ++h) qw[h] = buf_ld16(qrs, (uint32_t)(h * ga.sq_h * 2) + c * 16, 0);
+#pragma unroll
+        for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, (uint32_t)((rg + i * C::RG) * D * 2 + c * 16), 0);
+        if constexpr (!LATE_WK) {
+#pragma unroll
+            for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, (uint32_t)((rg + i * C::RG) * D * 2 + c * 16), 0);
+        }
+    }
+
+    __device__ __forceinline__ void finish(const GateArgs &ga, int b, int g, GateSmem<D> &sm) {
+        const int tid = threadIdx.x, c = tid % C::CH, rg = tid / C::CH;
+        const int dg = ga.dg, G = ga.G;
+        const uint16_t *qg = ga.q + b * ga.sq_b + (int64_t)(g * G) * ga.sq_h;
+        const auto wqrs = buffer_rsrc(ga.wq + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
+        const auto wkrs = buffer_rsrc(ga.wk + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
+        auto wrow = [&](int r) { return (uint32_t)(r * D * 2 + c * 16); };
+        if (tid < 256) {  // a[r] = Wq[r] . qbar, qbar the mean of the group's query heads
+            float qb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < QB; ++h) {
+                if (h < G) {
+                    float f[8];
+                    unpack8(qw[h], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qb[e] += f[e];
+                }
+            }
+            for (int h = QB; h < G; ++h) {  // groups wider than QB heads
+                float f[8];
+                unpack8(*reinterpret_cast<const uint4 *>(qg + h * ga.sq_h + c * 8), f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[e] += f[e];
+            }
+            const float inv_g = 1.0f / (float)G;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qb[e] *= inv_g;
+            for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {
+                if (r0 > 0) {
+#pragma unroll
+                    for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(r0 + rg + i * C::RG), 0);
+                }
+#pragma unroll
+                for (int i = 0; i < WB; ++i) {
+                    const int r = r0 + rg + i * C::RG;
+                    float f[8];
+                    unpack8(wqv[i], f);
+                    float s = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s = fmaf(f[e], qb[e], s);
+                    s = group_sum<C::CH>(s);  // all CH lanes of a row group share r
+                    if (c == 0 && r < dg) sm.a[r] = s;
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < 256) {  // u_part[rg] = sum over this thread's rows of a[r] Wk[r]
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {
+                if (r0 > 0 || LATE_WK) {
+#pragma unroll
+                    for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(r0 + rg + i * C::RG), 0);
+                }
+#pragma unroll
+                for (int i = 0; i < WB; ++i) {
+                    const int r = r0 + rg + i * C::RG;
+                    float f[8];
+                    unpack8(wkv[i], f);
+                    const float ar = r < dg ? sm.a[r] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = fmaf(ar, f[e], acc[e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.u_part[rg][c * 8 + e] = acc[e];
+        }
+        __syncthreads();
+        if (tid < D) {
+            float s = 0.f;
+#pragma unroll
+            for (int r = 0; r < C::RG; ++r) s += sm.u_part[r][tid];
+            sm.u[tid] = s * ga.gate_scale;
+        }
+        __syncthreads();
+    }
+};
+
 // Rows [jb, je) of the scores of pair = b * Hkv + g (je <= nb_max): u . kp_j
 // for the complete blocks among them, -inf for the rest.  Every thread of the
-// 256-thread workgroup calls it.  QB: query rows loaded up front (at least
+// NT-thread workgroup calls it.  QB: query rows loaded up front (at least
 // min(G, 8) keeps every row of a group of up to 8 in flight with the weights;
 // rows past QB are loaded when used).
-template <int D, class Mem, int QB = 8>
+template <int D, class Mem, int QB = 8, int NT = 256>
 __device__ __forceinline__ void gate_rows_item(const GateArgs &ga, int pair, int jb, int je, GateSmem<D> &sm) {
-    const uint16_t *q = ga.q;
-    const int64_t sq_b = ga.sq_b, sq_h = ga.sq_h;
-    const uint16_t *wq = ga.wq, *wk = ga.wk;
-    const int dg = ga.dg, G = ga.G, Hkv = ga.Hkv;
-    const float gate_scale = ga.gate_scale;
-    const float *kpool = ga.kpool;
-    const int nb_max = ga.nb_max, block_size = ga.block_size;
-    const int32_t *seqlens = ga.seqlens;
-    float *scores = ga.scores;
-    auto &a_s = sm.a;
-    auto &u_part = sm.u_part;
-    auto &u_s = sm.u;
-    using C = GateCfg<D>;
-    const int b = pair / Hkv, g = pair % Hkv;
+    using C = GateCfg<D, NT>;
+    const int nb_max = ga.nb_max;
+    const int b = pair / ga.Hkv, g = pair % ga.Hkv;
     const int tid = threadIdx.x, lr = tid / C::LPR, lc = tid % C::LPR;
-    int L = seqlens[b];
+    int L = ga.seqlens[b];
     L = L < 0 ? 0 : L;
-    int nc = L / block_size;
+    int nc = L / ga.block_size;
     nc = nc > nb_max ? nb_max : nc;
     const int jv = je < nc ? je : nc;  // rows [jb, jv) are complete blocks
-    float *srow = scores + (int64_t)pair * nb_max;
-    for (int j = (jb > jv ? jb : jv) + tid; j < je; j += 256) Mem::stf(srow + j, -INFINITY);
+    float *srow = ga.scores + (int64_t)pair * nb_max;
+    for (int j = (jb > jv ? jb : jv) + tid; j < je; j += NT) Mem::stf(srow + j, -INFINITY);
     if (jb >= jv) return;  // nothing complete here
 
-    // 1. Loads in the order they are used: the group's query rows and the first
-    // Wq and Wk rows (L2-resident), then this item's pooled-key rows.  A barrier
-    // between the two puts every wave's weight requests ahead of the pooled-key
-    // stream, so u is formed while the pooled rows are still arriving.  All go
-    // through buffer descriptors whose ranges end at the last valid row: rows
-    // past it (heads >= G, weight rows >= dg, blocks >= nc) read as zero, so no
-    // branch separates the loads and all of them stay in flight together.
-    const int c = tid % C::CH, rg = tid / C::CH;
-    constexpr int WB = 8;  // weight rows per thread in flight
-    const uint16_t *qg = q + b * sq_b + (int64_t)(g * G) * sq_h;
-    const auto qrs = buffer_rsrc(qg, (uint32_t)(((int64_t)(G - 1) * sq_h + D) * 2));
-    const auto wqrs = buffer_rsrc(wq + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
-    const auto wkrs = buffer_rsrc(wk + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
-    auto wrow = [&](int r) { return (uint32_t)(r * D * 2 + c * 16); };
-    uint4 qw[QB], wqv[WB], wkv[WB];
-#pragma unroll
-    for (int h = 0; h < QB; ++h) qw[h] = buf_ld16(qrs, (uint32_t)(h * sq_h * 2) + c * 16, 0);
-#pragma unroll
-    for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(rg + i * C::RG), 0);
-#pragma unroll
-    for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
+    // 1. Loads in the order they are used: the query rows and the first Wq and
+    // Wk rows (L2-resident), then this item's pooled-key rows (rows past jv read
+    // as zero).  A barrier between the two puts every wave's weight requests
+    // ahead of the pooled-key stream, so u is formed while the pooled rows are
+    // still arriving.
+    GateU<D, QB, (NT > 256)> gu;
+    gu.issue(ga, b, g);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)jv * D * 4);
+    const auto kprs = buffer_rsrc(ga.kpool + (int64_t)pair * nb_max * D, (uint32_t)jv * D * 4);
     float4 x[C::ITER];
 #pragma unroll
     for (int it = 0; it < C::ITER; ++it)
         x[it] = as_float4(buf_ld16_nt(kprs, (uint32_t)((jb + lr + it * C::ROWS) * D * 4 + lc * 16), 0));
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. u = gate_scale * Wk^T (Wq qbar) for (b, g).  Thread (c, rg) owns the
-    // 16-byte column chunk c of weight rows rg, rg + RG, ..., WB rows at a time.
-    float qb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < QB; ++h) {
-        if (h < G) {
-            float f[8];
-            unpack8(qw[h], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qb[e] += f[e];
-        }
-    }
-    for (int h = QB; h < G; ++h) {  // groups wider than QB heads
-        float f[8];
-        unpack8(*reinterpret_cast<const uint4 *>(qg + h * sq_h + c * 8), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[e] += f[e];
-    }
-    const float inv_g = 1.0f / (float)G;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qb[e] *= inv_g;
-    for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {  // a[r] = Wq[r] . qbar
-        if (r0 > 0) {
-#pragma unroll
-            for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(r0 + rg + i * C::RG), 0);
-        }
-#pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            const int r = r0 + rg + i * C::RG;
-            float f[8];
-            unpack8(wqv[i], f);
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s = fmaf(f[e], qb[e], s);
-            s = group_sum<C::CH>(s);  // all CH lanes of a row group share r
-            if (c == 0 && r < dg) a_s[r] = s;
-        }
-    }
-    __syncthreads();
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {  // u += a[r] * Wk[r]
-        if (r0 > 0) {
-#pragma unroll
-            for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(r0 + rg + i * C::RG), 0);
-        }
-#pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            const int r = r0 + rg + i * C::RG;
-            float f[8];
-            unpack8(wkv[i], f);
-            const float ar = r < dg ? a_s[r] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(ar, f[e], acc[e]);
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u_part[rg][c * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < D) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < C::RG; ++r) s += u_part[r][tid];
-        u_s[tid] = s * gate_scale;
-    }
-    __syncthreads();
+    // 2. u
+    gu.finish(ga, b, g, sm);
 
     // 3. score_j = u . kp_j, RPB rows at a time.
-    const float4 uu = reinterpret_cast<const float4 *>(u_s)[lc];
+    const float4 uu = reinterpret_cast<const float4 *>(sm.u)[lc];
     for (int j0 = jb;;) {
 #pragma unroll
         for (int it = 0; it < C::ITER; ++it) {

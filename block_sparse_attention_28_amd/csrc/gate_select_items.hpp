@@ -79,24 +79,19 @@ struct GateSelectArgs {
     int32_t *n_sel;      // [pairs]
 };
 
-// Every thread of the NT-thread workgroup calls it; keys: LDS scratch of nb_max
-// words.  G query heads per KV head; dg <= 256; KT the pooled keys' element type.
-template <int D, int G, int NT, class Mem, class KT = float>
-__device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int pair, GsSmem<D, NT> &sm,
-                                                 uint32_t *keys) {
+// sm.u = gate_scale * Wk^T (Wq qbar) of (b, g), qbar = mean of the group's
+// query heads.  Loads are issued q, Wq, Wk, then whatever issue_rows() issues
+// (the caller's pooled-key rows), so the dependent chain below (two small
+// products, three barriers) runs while those rows are still arriving.  Weight
+// rows past dg are clamped to the last one and masked, so no branch separates
+// the loads.  Every thread of the NT-thread workgroup calls it.
+template <int D, int G, int NT, class KT, class IssueRows>
+__device__ __forceinline__ void gate_u(const GateArgs &ga, int b, int g, GsSmem<D, NT> &sm,
+                                       IssueRows &&issue_rows) {
     using C = GsCfg<D, NT, G, KT>;
-    using KR = KRow<KT>;
-    const GateArgs &ga = gs.gate;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int Hkv = ga.Hkv, dg = ga.dg, nb_max = ga.nb_max;
-    const int b = pair / Hkv, g = pair % Hkv;
-    const int L = ga.seqlens[b];  // needed only once the scores exist
-
-    // 1. Loads: q chunk, first weight rows, first pooled-key rows.  Row indices
-    // past the data are clamped to its last row (their values are masked or
-    // discarded later), so no branch separates the loads, none waits for the
-    // context length, and all of them stay in flight together.
+    const int dg = ga.dg;
     const int c = tid % C::CH, rg = tid / C::CH;
     const auto qrs = buffer_rsrc(ga.q + b * ga.sq_b + (int64_t)(g * G) * ga.sq_h,
                                  (uint32_t)(((int64_t)(G - 1) * ga.sq_h + D) * 2));
@@ -112,16 +107,9 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
 #pragma unroll
     for (int i = 0; i < C::WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the u inputs first
-    const int lr = tid / C::LPR, lc = tid % C::LPR;
-    const KT *kpool = reinterpret_cast<const KT *>(ga.kpool);
-    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)nb_max * D * KR::KB);
-    auto krow = [&](int j) { return (uint32_t)((j < nb_max ? j : nb_max - 1) * D * KR::KB + lc * 16); };
-    uint4 x[C::ITER];
-#pragma unroll
-    for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(lr + it * C::ROWS), 0);
+    issue_rows();
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. u = gate_scale * Wk^T (Wq qbar), qbar = mean of the group's query heads.
     float qb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -153,7 +141,6 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
             if (c == 0 && r < dg) sm.a[r] = s;
         }
     }
-    block_select_prepare<NT>(sm.sel);  // ordered before the selection by the barriers below
     __syncthreads();
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -187,6 +174,34 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
         sm.u[tid] = s * ga.gate_scale;
     }
     __syncthreads();
+}
+
+// Every thread of the NT-thread workgroup calls it; keys: LDS scratch of nb_max
+// words.  G query heads per KV head; dg <= 256; KT the pooled keys' element type.
+template <int D, int G, int NT, class Mem, class KT = float>
+__device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int pair, GsSmem<D, NT> &sm,
+                                                 uint32_t *keys) {
+    using C = GsCfg<D, NT, G, KT>;
+    using KR = KRow<KT>;
+    const GateArgs &ga = gs.gate;
+    const int tid = threadIdx.x;
+    const int Hkv = ga.Hkv, nb_max = ga.nb_max;
+    const int b = pair / Hkv, g = pair % Hkv;
+    const int L = ga.seqlens[b];  // needed only once the scores exist
+
+    // 1-2. u, with the first pooled-key rows in flight behind its inputs.  Row
+    // indices past the table are clamped to its last row (their values are
+    // discarded later), so none of these loads waits for the context length.
+    const int lr = tid / C::LPR, lc = tid % C::LPR;
+    const KT *kpool = reinterpret_cast<const KT *>(ga.kpool);
+    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)nb_max * D * KR::KB);
+    auto krow = [&](int j) { return (uint32_t)((j < nb_max ? j : nb_max - 1) * D * KR::KB + lc * 16); };
+    uint4 x[C::ITER];
+    block_select_prepare<NT>(sm.sel);  // ordered before the selection by the barriers below
+    gate_u<D, G, NT, KT>(ga, b, g, sm, [&] {
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(lr + it * C::ROWS), 0);
+    });
 
     // 3. score_j = u . kp_j for the complete blocks, batch by batch; -inf after them.
     int nc = (L < 0 ? 0 : L) / ga.block_size;
@@ -224,6 +239,67 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
     const int k = block_select_keys<NT, Mem>(keys, nc, gs.pol, gs.k_max, gs.block_idx + (int64_t)pair * gs.k_max,
                                              nullptr, sm.sel);
     if (tid == 0) Mem::sti(gs.n_sel + pair, k);
+}
+
+}  // namespace seer
+
+namespace seer {
+
+// Scores of part `part` of `parts` of the rows of pair = b * Hkv + g: the
+// complete blocks are dealt evenly over the parts, the last part also writes
+// -inf for the rows past them.  The same arithmetic as gate_select_pair, so the
+// scores are bit for bit the ones seer_gate_select returns.  Every thread of
+// the NT-thread workgroup calls it.
+template <int D, int G, int NT, class Mem, class KT = float>
+__device__ __forceinline__ void gate_wide_rows(const GateArgs &ga, int pair, int part, int parts,
+                                               GsSmem<D, NT> &sm) {
+    using C = GsCfg<D, NT, G, KT>;
+    using KR = KRow<KT>;
+    const int tid = threadIdx.x;
+    const int Hkv = ga.Hkv, nb_max = ga.nb_max;
+    const int b = pair / Hkv, g = pair % Hkv;
+    int L = ga.seqlens[b];
+    L = L < 0 ? 0 : L;
+    int nc = L / ga.block_size;
+    nc = nc > nb_max ? nb_max : nc;
+    nc = __builtin_amdgcn_readfirstlane(nc);
+    const int jb = (int)((int64_t)part * nc / parts);
+    const int jv = (int)((int64_t)(part + 1) * nc / parts);  // rows [jb, jv) get scores
+    float *srow = ga.scores + (int64_t)pair * nb_max;
+    if (part == parts - 1)
+        for (int j = nc + tid; j < nb_max; j += NT) Mem::stf(srow + j, -INFINITY);
+    if (jb >= jv) return;
+    // Rows past jv read as zero (the descriptor's range ends there) and are not stored.
+    const int lr = tid / C::LPR, lc = tid % C::LPR;
+    const KT *kpool = reinterpret_cast<const KT *>(ga.kpool);
+    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)jv * D * KR::KB);
+    auto krow = [&](int j) { return (uint32_t)(j * D * KR::KB + lc * 16); };
+    uint4 x[C::ITER];
+    gate_u<D, G, NT, KT>(ga, b, g, sm, [&] {
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(jb + lr + it * C::ROWS), 0);
+    });
+    float uu[KR::EPL];
+#pragma unroll
+    for (int e = 0; e < KR::EPL; ++e) uu[e] = sm.u[lc * KR::EPL + e];
+    for (int j0 = jb;;) {
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it) {
+            const int j = j0 + lr + it * C::ROWS;
+            float s = KR::dot(uu, x[it]);
+            if constexpr (C::LPR == 8) {
+                s = group_sum<8>(s);
+            } else {
+                s = group_sum<16>(s);
+                if constexpr (C::LPR == 32) s = sum_xor16(s);
+            }
+            if (lc == 0 && j < jv) Mem::stf(srow + j, s);
+        }
+        j0 += C::RPB;
+        if (j0 >= jv) break;
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(j0 + lr + it * C::ROWS), 0);
+    }
 }
 
 }  // namespace seer
