@@ -123,7 +123,8 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, a.plan.out) and torch.equal(l1, a.plan.lse)
 
 
-@pytest.mark.parametrize("nc,k", [(16, 4), (512, 51), (2048, 64), (100, 99), (7, 3), (3000, 64)])
+@pytest.mark.parametrize("nc,k", [(16, 4), (512, 51), (2048, 64), (100, 99), (7, 3), (3000, 64), (5000, 1000),
+                                  (16128, 700)])
 def test_select_exact_with_ties(nc, k):
     """Selection on given scores, including exact integer ties: identical to the oracle's rule."""
     rng = np.random.default_rng(nc + k)

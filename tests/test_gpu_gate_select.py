@@ -90,3 +90,38 @@ def test_gate_select(case):
         # Exact ties really occurred (and were resolved toward the lower ids above).
         nc0 = min(int(seqlens[0]) // bs, nb_max)
         assert len(np.unique(sc[0, 0, :nc0])) <= rep
+
+
+# The standalone gate deals a pair's complete blocks over several 1024-thread
+# workgroups when there are few pairs: uneven shares, empty shares and
+# contexts shorter than one block.  name, B, Hq, Hkv, d, bs, nb_max, seqlens, dg, seed
+PART_CASES = [
+    ("many_parts_ragged", 2, 8, 2, 128, 64, 2048, [64 * 1000 + 5, 64 * 2048], 128, 71),
+    ("parts_with_empty_rows", 3, 6, 3, 128, 128, 1536, [0, 127, 128 * 1499 + 77], 96, 72),
+    ("group8_d64_parts", 1, 16, 2, 64, 64, 1000, [64 * 777 + 3], 64, 73),
+]
+
+
+@pytest.mark.parametrize("case", PART_CASES, ids=[c[0] for c in PART_CASES])
+def test_gate_scores_split_rows(case):
+    name, B, Hq, Hkv, d, bs, nb_max, lens, dg, seed = case
+    say(f"[gpu] gate_scores {name}")
+    x = inputs.gate_inputs(B, Hq, Hkv, d, dg, nb_max, seed, "cuda")
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    scores = torch.full((B, Hkv, nb_max), float("nan"), device="cuda")
+    gscale = 1.0 / math.sqrt(dg)
+    seer.seer_gate_scores(x["q"], x["wq"], x["wk"], x["kpool"], seqlens.cuda(), bs, gscale, scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().double().numpy()
+    q, wq, wk = host_bits(x["q"]), host_bits(x["wq"]), host_bits(x["wk"])
+    G = Hq // Hkv
+    for b in range(B):
+        nc = min(int(seqlens[b]) // bs, nb_max)
+        for g in range(Hkv):
+            assert np.all(np.isneginf(sc[b, g, nc:])), (b, g)
+            assert np.all(np.isfinite(sc[b, g, :nc])), (b, g)
+            if nc:
+                kp = x["kpool"][b, g, :nc].cpu().double().numpy()
+                _, S = oracle.gate_scores(q[b, g * G:(g + 1) * G], wq[g], wk[g], kp, gscale)
+                rel = np.abs(sc[b, g, :nc] - S).max() / max(np.abs(S).max(), 1e-30)
+                assert rel <= SCORE_REL, f"scores b={b} g={g}: rel err {rel}"
