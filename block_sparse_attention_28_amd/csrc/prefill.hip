@@ -376,17 +376,28 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // when the block's maximum exceeds it by more than kLazyRescale (log2
     // units), so the weights stay below 2^kLazyRescale and O is rarely
     // rescaled.  Any reference gives the same softmax once O is divided by l.
+    // m_ref[r] is m_run[r], or 0 while that is -inf.  Each lane first tests its
+    // own scores: rounding is monotone, so some lane's max * scale exceeds the
+    // bound exactly when the row's max * scale does, and the cross-lane
+    // reductions run only in the (rare) blocks where a reference moves.
     float m_ref[2] = {0.f, 0.f};
     auto prep = [&](const f32x4_t (&s)[2][2], bool live) {
+        float lmax[2];
+        bool need = false;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            float mloc = -INFINITY;
+            lmax[r] = -INFINITY;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mloc = fmax_fast(mloc, s[r][t][e]);
-            mloc = max_xor32(max_xor16(mloc)) * scale_log2;  // the 4 lanes of this query row; scale > 0
-            const bool bump = live && mloc > m_run[r] + kLazyRescale;  // always when m_run is still -inf
+                for (int e = 0; e < 4; ++e) lmax[r] = fmax_fast(lmax[r], s[r][t][e]);
+            need |= live && lmax[r] * scale_log2 > m_run[r] + kLazyRescale;  // always when m_run is still -inf
+        }
+        if (!__ballot(need)) return;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float mloc = max_xor32(max_xor16(lmax[r])) * scale_log2;  // the 4 lanes of this query row
+            const bool bump = live && mloc > m_run[r] + kLazyRescale;
             const float m_new = bump ? mloc : m_run[r];
             const float ref = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = bump ? fast_exp2(m_run[r] - ref) : 1.0f;

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(const StepArgs s) {
         __syncthreads();  // keys complete
         int32_t *kept = reinterpret_cast<int32_t *>(keys);
         int32_t *out = split == 0 ? const_cast<int32_t *>(s.dec.block_idx) + (int64_t)pair * s.k_max : nullptr;
-        const int k = block_select_keys<256, DeviceMem>(keys, nc, SelectPolicy{0, 1, 1, 0.f}, s.k_max, out,
+        const int k = block_select_keys<256, DeviceMem, 2>(keys, nc, SelectPolicy{0, 1, 1, 0.f}, s.k_max, out,
                                                         kept, sm.sel);
         if (split == 0 && threadIdx.x == 0) DeviceMem::sti(const_cast<int32_t *>(s.dec.n_sel) + pair, k);
         __syncthreads();  // kept ids complete; the selection's LDS is free for the decode tiles

@@ -42,7 +42,8 @@ __device__ __forceinline__ void block_select_prepare(SelBlockSmem<NT> &sm) {
 // Returns k, the same in every thread.  Every thread of the NT-thread
 // workgroup calls it; the caller orders `kept` before its readers with a
 // barrier.
-template <int NT, class Mem>
+// KR: keys per thread held in registers (ids tid + NT i, i < KR) for every pass.
+template <int NT, class Mem, int KR = 8>
 __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, const SelectPolicy &pol, int k_max,
                                                  int32_t *out, int32_t *kept, SelBlockSmem<NT> &sm) {
     constexpr int NW = NT / 64;
@@ -86,6 +87,14 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
             for (int i = tid; i < k; i += NT) kept[i] = i;
         return k;
     }
+    // Each thread's first KR keys (ids tid + NT i) stay in registers for every
+    // pass and the sweep; keys past KR NT are read from LDS each time.
+    uint32_t kreg[KR];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const int j = tid + i * NT;
+        kreg[i] = j < nc ? keys[j] : 0u;
+    }
     uint32_t prefix = 0;
     int need = k;  // keys still to take among those matching `prefix` so far
 #pragma unroll
@@ -94,7 +103,10 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
         const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
         int *hist = sm.hist[pass % 3];
         if (tid < 256) sm.hist[(pass + 1) % 3][tid] = 0;
-        for (int j = tid; j < nc; j += NT) {
+#pragma unroll
+        for (int i = 0; i < KR; ++i)
+            if (tid + i * NT < nc && (kreg[i] & hi_mask) == prefix) atomicAdd(&hist[(kreg[i] >> shift) & 255u], 1);
+        for (int j = tid + KR * NT; j < nc; j += NT) {
             const uint32_t key = keys[j];
             if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
         }
@@ -126,9 +138,13 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
     // Keep keys > T and the first `need` keys == T in id order.
     const uint32_t T = prefix;
     int gt_seen = 0, eq_seen = 0;
-    for (int base = 0, round = 0; base < nc; base += NT, round ^= 1) {
+    for (int base = 0, round = 0, i = 0; base < nc; base += NT, round ^= 1, ++i) {
         const int j = base + tid;
-        const uint32_t key = j < nc ? keys[j] : 0u;
+        uint32_t key = 0u;
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+            if (i == r) key = kreg[r];
+        if (i >= KR) key = j < nc ? keys[j] : 0u;
         const bool gt = j < nc && key > T, eq = j < nc && key == T;
         const uint64_t gt_mask = __ballot(gt), eq_mask = __ballot(eq);
         if (lane == 0) {
