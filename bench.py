@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0 = skip)")
     ap.add_argument("--cpu-sequences", type=int, default=2)
     ap.add_argument("--prefill-steps", type=int, default=5, help="block-sparse prefill timing (0 = skip)")
-    ap.add_argument("--mode", default="gate_select", choices=("gate_select", "calls", "fused"),
+    ap.add_argument("--mode", default="calls", choices=("gate_select", "calls", "fused"),
                     help="form of the timed step (the others are timed briefly for context)")
     ap.add_argument("--mode-steps", type=int, default=16, help="steps per form in the context timing (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=16, help="HIP-graph replays timed (0 = skip)")
@@ -103,9 +103,10 @@ def gate_bytes(w, seqlens_host):
 
 
 def graph_step_us(plan, layers, steps, w, args):
-    """The gate_select + decode step captured once per layer as a HIP graph, then replayed.
-    Each replay's output is checked against the eager step's."""
+    """The step in its timed form (gate, select, decode) captured once per layer as a HIP graph,
+    then replayed.  Each replay's output is checked against the eager step's."""
     R = len(layers)
+    mode = "gate_select" if args.mode == "gate_select" else "calls"
     g_q = torch.empty_like(steps[0]["q"])
     g_sl = torch.empty_like(steps[0]["seqlens"])
     graphs = []
@@ -116,15 +117,13 @@ def graph_step_us(plan, layers, steps, w, args):
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            plan.gate_select(g_q, c["wq"], c["wk"], layers[l].kpool, g_sl)
-            plan.decode(g_q, c["k"], c["v"], g_sl)
+            plan.step(g_q, c["k"], c["v"], g_sl, layers[l].kpool, c["wq"], c["wk"], mode=mode)
         graphs.append(g)
     # replay vs eager on the first steps
     for s in range(min(R, 4)):
         lay = layers[steps[s]["layer"]]
         c = lay.cache
-        plan.gate_select(steps[s]["q"], c["wq"], c["wk"], lay.kpool, steps[s]["seqlens"])
-        plan.decode(steps[s]["q"], c["k"], c["v"], steps[s]["seqlens"])
+        plan.step(steps[s]["q"], c["k"], c["v"], steps[s]["seqlens"], lay.kpool, c["wq"], c["wk"], mode=mode)
         torch.cuda.synchronize()
         ref = plan.out.clone()
         g_q.copy_(steps[s]["q"])
