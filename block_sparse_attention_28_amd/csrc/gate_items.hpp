@@ -229,11 +229,4 @@ __device__ __forceinline__ void gate_rows_item(const GateArgs &ga, int pair, int
     }
 }
 
-// Rows [chunk * RPB, (chunk + 1) * RPB) of the scores of pair = b * Hkv + g.
-template <int D, class Mem, int QB = 8>
-__device__ __forceinline__ void gate_chunk_item(const GateArgs &ga, int chunk, int pair, GateSmem<D> &sm) {
-    const int jb = chunk * GateCfg<D>::RPB, je = jb + GateCfg<D>::RPB;
-    gate_rows_item<D, Mem, QB>(ga, pair, jb, je < ga.nb_max ? je : ga.nb_max, sm);
-}
-
 }  // namespace seer

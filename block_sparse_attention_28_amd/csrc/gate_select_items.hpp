@@ -1,9 +1,9 @@
 // gate_select_items.hpp -- gate scores and token-budget selection of one
 // (b, KV head) by one workgroup.
 //
-// Same operation as gate_chunk_item over all rows of a pair followed by
-// select_pair_item (see gate_items.hpp and topk_wave.hpp for the definitions
-// this follows), arranged so that the scores never leave the workgroup:
+// Same operation as gate_rows_item over all rows of a pair followed by the
+// selection (see gate_items.hpp and topk_wave.hpp for the definitions this
+// follows), arranged so that the scores never leave the workgroup:
 //
 //  1. Loads are issued in the order q, Wq, Wk, pooled keys.  The gate vector
 //     u = gate_scale * Wk^T (Wq qbar) only needs the first three, so its
@@ -243,63 +243,3 @@ __device__ __forceinline__ void gate_select_pair(const GateSelectArgs &gs, int p
 
 }  // namespace seer
 
-namespace seer {
-
-// Scores of part `part` of `parts` of the rows of pair = b * Hkv + g: the
-// complete blocks are dealt evenly over the parts, the last part also writes
-// -inf for the rows past them.  The same arithmetic as gate_select_pair, so the
-// scores are bit for bit the ones seer_gate_select returns.  Every thread of
-// the NT-thread workgroup calls it.
-template <int D, int G, int NT, class Mem, class KT = float>
-__device__ __forceinline__ void gate_wide_rows(const GateArgs &ga, int pair, int part, int parts,
-                                               GsSmem<D, NT> &sm) {
-    using C = GsCfg<D, NT, G, KT>;
-    using KR = KRow<KT>;
-    const int tid = threadIdx.x;
-    const int Hkv = ga.Hkv, nb_max = ga.nb_max;
-    const int b = pair / Hkv, g = pair % Hkv;
-    int L = ga.seqlens[b];
-    L = L < 0 ? 0 : L;
-    int nc = L / ga.block_size;
-    nc = nc > nb_max ? nb_max : nc;
-    nc = __builtin_amdgcn_readfirstlane(nc);
-    const int jb = (int)((int64_t)part * nc / parts);
-    const int jv = (int)((int64_t)(part + 1) * nc / parts);  // rows [jb, jv) get scores
-    float *srow = ga.scores + (int64_t)pair * nb_max;
-    if (part == parts - 1)
-        for (int j = nc + tid; j < nb_max; j += NT) Mem::stf(srow + j, -INFINITY);
-    if (jb >= jv) return;
-    // Rows past jv read as zero (the descriptor's range ends there) and are not stored.
-    const int lr = tid / C::LPR, lc = tid % C::LPR;
-    const KT *kpool = reinterpret_cast<const KT *>(ga.kpool);
-    const auto kprs = buffer_rsrc(kpool + (int64_t)pair * nb_max * D, (uint32_t)jv * D * KR::KB);
-    auto krow = [&](int j) { return (uint32_t)(j * D * KR::KB + lc * 16); };
-    uint4 x[C::ITER];
-    gate_u<D, G, NT, KT>(ga, b, g, sm, [&] {
-#pragma unroll
-        for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(jb + lr + it * C::ROWS), 0);
-    });
-    float uu[KR::EPL];
-#pragma unroll
-    for (int e = 0; e < KR::EPL; ++e) uu[e] = sm.u[lc * KR::EPL + e];
-    for (int j0 = jb;;) {
-#pragma unroll
-        for (int it = 0; it < C::ITER; ++it) {
-            const int j = j0 + lr + it * C::ROWS;
-            float s = KR::dot(uu, x[it]);
-            if constexpr (C::LPR == 8) {
-                s = group_sum<8>(s);
-            } else {
-                s = group_sum<16>(s);
-                if constexpr (C::LPR == 32) s = sum_xor16(s);
-            }
-            if (lc == 0 && j < jv) Mem::stf(srow + j, s);
-        }
-        j0 += C::RPB;
-        if (j0 >= jv) break;
-#pragma unroll
-        for (int it = 0; it < C::ITER; ++it) x[it] = buf_ld16_nt(kprs, krow(j0 + lr + it * C::ROWS), 0);
-    }
-}
-
-}  // namespace seer

@@ -86,20 +86,6 @@ __device__ __forceinline__ void wave_load_keys(const float *scores, int n, uint3
     wave_lds_sync();
 }
 
-// Number of keys[0..n) whose softmax probability is at least tau, by one wave.
-__device__ __forceinline__ int wave_threshold_count(const uint32_t *keys, int n, float tau, int lane) {
-    float m = -INFINITY;
-    for (int j = lane; j < n; j += 64) m = fmax_fast(m, key_to_float(keys[j]));
-    m = wave_max(m);
-    float z = 0.f;
-    for (int j = lane; j < n; j += 64) z += expf(key_to_float(keys[j]) - m);
-    z = wave_sum(z);
-    const float bar = tau * z;
-    int c = 0;
-    for (int j = lane; j < n; j += 64) c += expf(key_to_float(keys[j]) - m) >= bar ? 1 : 0;
-    return (int)wave_sum((float)c);
-}
-
 // Select the k largest of the n keys in LDS (0 < k < n), write their ids
 // ascending to out[0..k) through Mem.  hist: LDS scratch of 256 words private
 // to this wave.  Every lane of the wave must call it.
@@ -170,39 +156,6 @@ __device__ __forceinline__ void wave_topk_ascending(const float *scores, int n, 
                                                     int32_t *out, int lane) {
     wave_load_keys<Mem>(scores, n, keys, lane);
     wave_topk_from_keys<Mem>(n, k, keys, hist, out, lane);
-}
-
-// Selection of one (b, head) = pair by one wave: k blocks by the policy
-// (ties to the lower id), ascending in block_idx[pair][0..k), -1 after, and
-// n_sel[pair] = k.
-template <class Mem>
-__device__ __forceinline__ void select_pair_item(const float *scores, const int32_t *seqlens, int H, int nb_max,
-                                                 int block_size, int k_max, int32_t *block_idx, int32_t *n_sel,
-                                                 int pair, uint32_t *keys, int *hist, int lane,
-                                                 const SelectPolicy pol = SelectPolicy{0, 1, 1, 0.f}) {
-    const int b = pair / H;
-    int L = seqlens[b];
-    L = L < 0 ? 0 : L;
-    int nc = L / block_size;
-    nc = nc > nb_max ? nb_max : nc;
-    int k = policy_count(pol, nc, k_max);
-    const float *row = scores + (int64_t)pair * nb_max;
-    bool loaded = false;
-    if (pol.kind == 2 && k > 0) {
-        wave_load_keys<Mem>(row, nc, keys, lane);
-        loaded = true;
-        const int c = wave_threshold_count(keys, nc, pol.tau, lane);
-        k = c < k ? c : k;
-    }
-    int32_t *out = block_idx + (int64_t)pair * k_max;
-    if (k == nc || k == 0) {  // every complete block, or none, is kept
-        for (int i = lane; i < k_max; i += 64) Mem::sti(out + i, i < k ? i : -1);
-    } else {
-        if (!loaded) wave_load_keys<Mem>(row, nc, keys, lane);
-        wave_topk_from_keys<Mem>(nc, k, keys, hist, out, lane);
-        for (int i = k + lane; i < k_max; i += 64) Mem::sti(out + i, -1);
-    }
-    if (lane == 0) Mem::sti(n_sel + pair, k);
 }
 
 }  // namespace seer
