@@ -57,41 +57,47 @@ struct GateSmem {
     float u[D];
 };
 
-// The gate vector u = gate_scale * Wk^T (Wq qbar) of (b, g), formed by the
-// first 256 threads of the workgroup: thread t owns the 16-byte column chunk
-// t % CH of weight rows t / CH + RG i.  issue() starts the loads of the query
-// rows and of the first Wq and Wk rows (threads >= 256 issue nothing), through
-// buffer descriptors whose ranges end at the last valid row, so heads >= G and
-// weight rows >= dg read as zero and no branch separates the loads.  finish()
-// leaves u in sm.u; every thread of the workgroup calls it (it holds barriers).
-// Workgroups of any size >= 256 therefore form u in the same order, bit for bit.
-// LATE_WK: load the Wk rows only once a is formed (fewer registers held while
-// the pooled rows are in flight, one more L2 round trip on u's path).
-template <int D, int QB, bool LATE_WK = false>
+// The gate vector u = gate_scale * Wk^T (Wq qbar) of (b, g) in one fixed
+// order: "thread" t < 256 owns the 16-byte column chunk t % CH of weight rows
+// t / CH + RG i; it forms a[r] = Wq[r] . qbar for its Wq rows, then its share
+// u_part[t / CH] of Wk^T a over its Wk rows.  issue() starts the loads of the
+// query rows and of the first Wq and Wk rows, through buffer descriptors whose
+// ranges end at the last valid row, so heads >= G and weight rows >= dg read as
+// zero and no branch separates the loads.  finish() leaves u in sm.u; every
+// thread of the workgroup calls it (it holds barriers).  With SPLIT (workgroups
+// of 512 threads or more) thread 256 + t holds t's Wk rows and does its Wk
+// share, so every weight row is in flight from the start without one thread
+// holding both; the arithmetic, and hence u, is the same bit for bit.
+template <int D, int QB, bool SPLIT = false>
 struct GateU {
     using C = GateCfg<D>;
     static constexpr int WB = 8;  // weight rows per thread in flight
-    uint4 qw[QB], wqv[WB], wkv[WB];
+    uint4 qw[QB], wv[WB], wkv[SPLIT ? 1 : WB];  // wv: Wq rows (threads < 256), or Wk rows (SPLIT, 256..511)
 
     __device__ __forceinline__ void issue(const GateArgs &ga, int b, int g) {
-        const int tid = threadIdx.x, c = tid % C::CH, rg = tid / C::CH;
-        if (tid >= 256) return;
+        const int tid = threadIdx.x, t = tid & 255, c = t % C::CH, rg = t / C::CH;
         const uint16_t *qg = ga.q + b * ga.sq_b + (int64_t)(g * ga.G) * ga.sq_h;
         const auto qrs = buffer_rsrc(qg, (uint32_t)(((int64_t)(ga.G - 1) * ga.sq_h + D) * 2));
         const auto wqrs = buffer_rsrc(ga.wq + (int64_t)g * ga.dg * D, (uint32_t)(ga.dg * D * 2));
         const auto wkrs = buffer_rsrc(ga.wk + (int64_t)g * ga.dg * D, (uint32_t)(ga.dg * D * 2));
+        auto wrow = [&](int r) { return (uint32_t)(r * D * 2 + c * 16); };
+        if (tid < 256) {
 #pragma unroll
-        for (int h = 0; h < QB; ++h) qw[h] = buf_ld16(qrs, (uint32_t)(h * ga.sq_h * 2) + c * 16, 0);
+            for (int h = 0; h < QB; ++h) qw[h] = buf_ld16(qrs, (uint32_t)(h * ga.sq_h * 2) + c * 16, 0);
 #pragma unroll
-        for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, (uint32_t)((rg + i * C::RG) * D * 2 + c * 16), 0);
-        if constexpr (!LATE_WK) {
+            for (int i = 0; i < WB; ++i) wv[i] = buf_ld16(wqrs, wrow(rg + i * C::RG), 0);
+            if constexpr (!SPLIT) {
 #pragma unroll
-            for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, (uint32_t)((rg + i * C::RG) * D * 2 + c * 16), 0);
+                for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
+            }
+        } else if (SPLIT && tid < 512) {
+#pragma unroll
+            for (int i = 0; i < WB; ++i) wv[i] = buf_ld16(wkrs, wrow(rg + i * C::RG), 0);
         }
     }
 
     __device__ __forceinline__ void finish(const GateArgs &ga, int b, int g, GateSmem<D> &sm) {
-        const int tid = threadIdx.x, c = tid % C::CH, rg = tid / C::CH;
+        const int tid = threadIdx.x, t = tid & 255, c = t % C::CH, rg = t / C::CH;
         const int dg = ga.dg, G = ga.G;
         const uint16_t *qg = ga.q + b * ga.sq_b + (int64_t)(g * G) * ga.sq_h;
         const auto wqrs = buffer_rsrc(ga.wq + (int64_t)g * dg * D, (uint32_t)(dg * D * 2));
@@ -120,13 +126,13 @@ struct GateU {
             for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {
                 if (r0 > 0) {
 #pragma unroll
-                    for (int i = 0; i < WB; ++i) wqv[i] = buf_ld16(wqrs, wrow(r0 + rg + i * C::RG), 0);
+                    for (int i = 0; i < WB; ++i) wv[i] = buf_ld16(wqrs, wrow(r0 + rg + i * C::RG), 0);
                 }
 #pragma unroll
                 for (int i = 0; i < WB; ++i) {
                     const int r = r0 + rg + i * C::RG;
                     float f[8];
-                    unpack8(wqv[i], f);
+                    unpack8(wv[i], f);
                     float s = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) s = fmaf(f[e], qb[e], s);
@@ -136,18 +142,20 @@ struct GateU {
             }
         }
         __syncthreads();
-        if (tid < 256) {  // u_part[rg] = sum over this thread's rows of a[r] Wk[r]
+        // u_part[rg] = sum over t's Wk rows of a[r] Wk[r], by thread t or (SPLIT) 256 + t
+        if (SPLIT ? (tid >= 256 && tid < 512) : tid < 256) {
+            uint4 *wk_rows = SPLIT ? wv : wkv;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int r0 = 0; r0 < dg; r0 += WB * C::RG) {
-                if (r0 > 0 || LATE_WK) {
+                if (r0 > 0) {
 #pragma unroll
-                    for (int i = 0; i < WB; ++i) wkv[i] = buf_ld16(wkrs, wrow(r0 + rg + i * C::RG), 0);
+                    for (int i = 0; i < WB; ++i) wk_rows[i] = buf_ld16(wkrs, wrow(r0 + rg + i * C::RG), 0);
                 }
 #pragma unroll
                 for (int i = 0; i < WB; ++i) {
                     const int r = r0 + rg + i * C::RG;
                     float f[8];
-                    unpack8(wkv[i], f);
+                    unpack8(wk_rows[i], f);
                     const float ar = r < dg ? sm.a[r] : 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[e] = fmaf(ar, f[e], acc[e]);
@@ -192,7 +200,7 @@ __device__ __forceinline__ void gate_rows_item(const GateArgs &ga, int pair, int
     // as zero).  A barrier between the two puts every wave's weight requests
     // ahead of the pooled-key stream, so u is formed while the pooled rows are
     // still arriving.
-    GateU<D, QB, (NT > 256)> gu;
+    GateU<D, QB, (NT >= 512)> gu;
     gu.issue(ga, b, g);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
