@@ -9,7 +9,9 @@ namespace seer {
 
 // One 1024-thread workgroup per part of a pair: the pair's complete blocks
 // are dealt evenly over `parts` workgroups (the last one also writes -inf past
-// them).  u is formed by the first 256 threads as in every other gate body.
+// them).  u is formed in GateU's one fixed order, as in every other gate body
+// (here threads 256..511 hold the Wk rows), so the scores match the fused
+// step's bit for bit.
 template <int D, int QB>
 __global__ __launch_bounds__(1024) void gate_scores_kernel(const GateArgs ga, int parts) {
     __shared__ GateSmem<D> sm;

@@ -11,11 +11,11 @@
 // so each workgroup forms u = gate_scale * Wk^T (Wq qbar) for its (b, g) and
 // then streams fp32 pooled keys once: score_j = u . kp_j.
 //
-// A work item owns RPB consecutive pooled-key rows of one (b, g): it issues
-// the loads of the query rows and gate weights (L2-resident) and then all of
-// its pooled-key rows (16 bytes per lane, 16 rows in flight per thread), forms
-// u while the pooled rows arrive, then finishes the dot products with 32-lane
-// DPP/permlane reductions.
+// A work item owns a range of pooled-key rows of one (b, g): it issues the
+// loads of the query rows and gate weights (L2-resident), then a batch of RPB
+// pooled-key rows (16 bytes per lane, ITER rows in flight per thread), forms u
+// while the pooled rows arrive, then finishes the dot products with 32-lane
+// DPP/permlane reductions, batch after batch.
 #pragma once
 
 #include "seer_device.hpp"

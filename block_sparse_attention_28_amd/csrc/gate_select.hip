@@ -2,10 +2,12 @@
 // (seer_gate_select): one 1024-thread workgroup per (b, KV head).
 //
 // With at least a quarter as many (b, KV head) pairs as compute units, one
-// workgroup per pair streams the pooled keys about as fast as the chunked gate
-// kernel, and the selection then runs on scores held in LDS instead of in a
-// second launch.  With fewer pairs, or shapes outside the limits of the
-// one-workgroup form, the call runs seer_gate_scores and seer_select_blocks.
+// workgroup per pair streams the pair's pooled keys and selects from the
+// scores held in LDS, with no second launch.  One workgroup per pair keeps
+// only that many compute units streaming, so this form takes about as long as
+// seer_gate_scores (every compute unit streams) plus seer_select_blocks.  With
+// fewer pairs, or shapes outside the limits of the one-workgroup form, the
+// call runs those two.
 #include "gate_select_items.hpp"
 #include "seer_host.hpp"
 

@@ -1,7 +1,7 @@
 // step.hip -- one gated sparse decode step in a single persistent launch.
 //
 // The same work as seer_gate_scores + seer_select_blocks + seer_sparse_decode
-// (gate chunks, per-(b, KV head) selection, decode splits, log-sum-exp merges;
+// (gate rows, per-(b, KV head) selection, decode splits, log-sum-exp merges;
 // see gate_items.hpp, topk_block.hpp and decode_items.hpp for the operation),
 // but run by one grid of resident workgroups: workgroup w takes work items
 // w, w + grid, w + 2 grid, ... in increasing order.  Item (pair, split) for
