@@ -13,7 +13,7 @@ memory (as the layers of a model do); with inputs resident in HBM, the value
 is effective KV bandwidth: bytes of the kept K/V blocks (plus tail, query,
 output and ids) per step divided by the measured step time.
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -282,7 +282,7 @@ def per_head_context(w, lay, step, plan, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench needs a GPU"

@@ -55,7 +55,7 @@ def rand_case(G, d, L, seed):
 
 @pytest.mark.parametrize("G,d,L,bs", [(4, 64, 300, 64), (1, 128, 256, 128), (8, 64, 1000, 64), (2, 32, 7, 64)])
 def test_all_blocks_selected_equals_dense_attention(G, d, L, bs):
-    """spec check (1): every block selected -> plain dense softmax attention."""
+    """Pin: every block selected -> plain dense softmax attention."""
     q, k, v = rand_case(G, d, L, seed=G * 1000 + L)
     scale = 1.0 / math.sqrt(d)
     idx = np.arange(L // bs, dtype=np.int32)
@@ -83,7 +83,7 @@ def test_sparse_equals_masked_dense(seed):
     ref_out, ref_lse = sdpa_reference(q, k, v, mask, scale)
     np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
-    # spec check (2): softmax weights sum to one, and vanish outside T
+    # pin: softmax weights sum to one, and vanish outside T
     np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
     assert np.all(w[:, ~mask.numpy()] == 0.0)
 

@@ -116,7 +116,7 @@ def _dominant_subsets(scores, k):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_selection_brute_force(seed):
-    """spec check (4): exactly one k-subset dominates the rest; it is the oracle's, and
+    """Pin (brute force): exactly one k-subset dominates the rest; it is the oracle's, and
     it has the largest score sum of all k-subsets."""
     rng = np.random.default_rng(seed)
     n = int(rng.integers(1, 13))
@@ -127,7 +127,7 @@ def test_selection_brute_force(seed):
         scores = rng.standard_normal(n)
     sel = oracle.select_blocks(scores, k)
     m = min(k, n)
-    assert len(sel) == m                                   # spec check (3)
+    assert len(sel) == m                                   # pin: the count is min(k, nc)
     dom = _dominant_subsets(scores, m)
     assert len(dom) == 1 and tuple(sel.tolist()) == dom[0]
     best = max(sum(scores[list(s)]) for s in itertools.combinations(range(n), m)) if m else 0.0
