@@ -143,7 +143,7 @@ def test_selection_ties_go_to_lower_index_and_output_ascends():
 
 
 def test_selection_counts_golden():
-    """spec check (3) at the budgets/blocks of the decode workloads (tests/golden)."""
+    """Pin: selected counts at the budgets and block sizes of the decode workloads (tests/golden)."""
     rows = [list(map(int, ln.split())) for ln in open(os.path.join(GOLDEN, "selection_counts.txt"))
             if ln.strip() and not ln.startswith("#")]
     rng = np.random.default_rng(0)

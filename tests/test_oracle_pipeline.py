@@ -51,7 +51,7 @@ def test_tiny_workload_selects_four_of_sixteen():
     c = {k: (inputs.bf16_bits(t) if t.dtype == torch.bfloat16 else t.numpy()) for k, t in cache.items()}
     q = inputs.bf16_bits(inputs.decode_query(w, 0, "cpu"))
     r, _ = run_step(w, c, q)
-    assert r["n_sel"].tolist() == [[4]]                     # spec check (3)
+    assert r["n_sel"].tolist() == [[4]]                     # pin: count = budget / block size
     assert np.all(np.diff(r["idx"][0, 0]) > 0)
     assert np.isfinite(r["out"]).all()
 
@@ -81,7 +81,8 @@ def test_batched_step_composes_stage_functions():
 
 
 def test_budget_covering_context_is_dense_gqa_attention():
-    """spec check (1) through the whole decode step, with GQA and a ragged tail."""
+    """Pin: every block selected equals dense attention through the whole decode step, with GQA
+    and a ragged tail."""
     w, c, q = small_decode(L_range=(130, 600), seed=12)
     r, _ = run_step(w, c, q, budget=10 ** 6)
     for b in range(w.B):
