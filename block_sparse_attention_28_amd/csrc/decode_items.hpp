@@ -451,6 +451,15 @@ template <int D, class Mem>
 __device__ __forceinline__ void decode_merge_row(const float *part_o, const float2 *part_ml, int S, int64_t bh,
                                                  void *out, int out_dtype, float *lse, MergeSmem &sm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The first PRE partial rows do not depend on (m, l): they are requested
+    // together with them, one memory round trip instead of two.
+    constexpr int PRE = 8;
+    const float *po = part_o + bh * S * D + (tid < D ? tid : 0);
+    float x0[PRE];
+    if (tid < D) {
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) x0[i] = i < S ? Mem::ldf(po + (int64_t)i * D) : 0.f;
+    }
     float2 v = make_float2(-INFINITY, 0.f);
     if (tid < S) v = Mem::ldf2(part_ml + bh * S + tid);
     float M = wave_max(v.x);
@@ -465,9 +474,11 @@ __device__ __forceinline__ void decode_merge_row(const float *part_o, const floa
     __syncthreads();
     Ls = sm.red[1][0] + sm.red[1][1];
     if (tid < D) {
-        const float *po = part_o + bh * S * D + tid;
         float O = 0.f;
-        int sp = 0;
+#pragma unroll
+        for (int i = 0; i < PRE; ++i)
+            if (i < S) O = fmaf(x0[i], sm.w[i], O);
+        int sp = PRE;
         for (; sp + 8 <= S; sp += 8) {
             float x[8];
 #pragma unroll
