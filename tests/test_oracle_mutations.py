@@ -82,6 +82,12 @@ MUTATIONS = [
      lambda: T_gt.test_prefill_mass_equals_torch_causal_softmax(300, 64)),
     ("prefill causal mask dropped", "for (int tt = 0; tt <= t; ++tt)", "for (int tt = 0; tt < L; ++tt)",
      lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
+    ("query group of KV head g taken at g, not g * G", "const uint16_t *qg = q + b * sq_b + (int64_t)g * G * sq_h;",
+     "const uint16_t *qg = q + b * sq_b + (int64_t)g * sq_h;", T_pipe.test_budget_covering_context_is_dense_gqa_attention),
+    ("gate scale dropped", "            s *= gate_scale;\n", "            (void)gate_scale;\n",
+     lambda: T_gs.test_gate_matches_reassociated_form(4, 64, 32)),
+    ("lse in log2 units", "        lse[h] = m + log(denom);", "        lse[h] = m + log2(denom);",
+     lambda: T_att.test_all_blocks_selected_equals_dense_attention(4, 64, 300, 64)),
 ]
 
 
