@@ -140,6 +140,8 @@ def test_selection_ties_go_to_lower_index_and_output_ascends():
     scores = np.array([1.0, 3.0, 3.0, 0.5, 3.0, 2.0])
     np.testing.assert_array_equal(oracle.select_blocks(scores, 2), [1, 2])
     np.testing.assert_array_equal(oracle.select_blocks(scores, 4), [1, 2, 4, 5])
+    # ids come out ascending, not in score order (9 then 5)
+    np.testing.assert_array_equal(oracle.select_blocks(np.array([5.0, 1.0, 4.0, 9.0]), 2), [0, 3])
 
 
 def test_selection_counts_golden():

@@ -88,6 +88,10 @@ MUTATIONS = [
      lambda: T_gs.test_gate_matches_reassociated_form(4, 64, 32)),
     ("lse in log2 units", "        lse[h] = m + log(denom);", "        lse[h] = m + log2(denom);",
      lambda: T_att.test_all_blocks_selected_equals_dense_attention(4, 64, 300, 64)),
+    ("kept ids left in score order", "    qsort(idx, (size_t)n, sizeof(int32_t), by_index);",
+     "    (void)by_index;", T_gs.test_selection_ties_go_to_lower_index_and_output_ascends),
+    ("prefill row keeps the previous block instead of its diagonal", "        dst[n] = i;",
+     "        dst[n] = i > 0 ? i - 1 : i;", lambda: T_pipe.test_prefill_rows_keep_diagonal_and_k_i_blocks((1, 10))),
 ]
 
 
