@@ -92,6 +92,11 @@ MUTATIONS = [
      "    (void)by_index;", T_gs.test_selection_ties_go_to_lower_index_and_output_ascends),
     ("prefill row keeps the previous block instead of its diagonal", "        dst[n] = i;",
      "        dst[n] = i > 0 ? i - 1 : i;", lambda: T_pipe.test_prefill_rows_keep_diagonal_and_k_i_blocks((1, 10))),
+    ("pooled cache of every KV head taken from head 0", "so_pool_k(k + b * sk_b + g * sk_h, sk_t,",
+     "so_pool_k(k + b * sk_b, sk_t,", T_pipe.test_batched_step_composes_stage_functions),
+    ("decode output of KV head g written at row g, not g * G",
+     "out + ((int64_t)b * Hq + (int64_t)g * G) * d,", "out + ((int64_t)b * Hq + (int64_t)g) * d,",
+     T_pipe.test_budget_covering_context_is_dense_gqa_attention),
 ]
 
 
