@@ -97,6 +97,10 @@ MUTATIONS = [
     ("decode output of KV head g written at row g, not g * G",
      "out + ((int64_t)b * Hq + (int64_t)g * G) * d,", "out + ((int64_t)b * Hq + (int64_t)g) * d,",
      T_pipe.test_budget_covering_context_is_dense_gqa_attention),
+    ("prefill partial block pooled over bs rows", "        dst[c] = sum / (t1 - t0);", "        dst[c] = sum / bs;",
+     T_pipe.test_prefill_partial_last_block_pools_existing_rows),
+    ("prefill gate pools Q for the key side", "        pool_block_rows(k, row_stride, L, d, bs, i, kbar);",
+     "        pool_block_rows(q, row_stride, L, d, bs, i, kbar);", T_pipe.test_prefill_partial_last_block_pools_existing_rows),
 ]
 
 
