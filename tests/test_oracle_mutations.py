@@ -101,6 +101,8 @@ MUTATIONS = [
      T_pipe.test_prefill_partial_last_block_pools_existing_rows),
     ("prefill gate pools Q for the key side", "        pool_block_rows(k, row_stride, L, d, bs, i, kbar);",
      "        pool_block_rows(q, row_stride, L, d, bs, i, kbar);", T_pipe.test_prefill_partial_last_block_pools_existing_rows),
+    ("a kept block's last token left out", "for (int t = idx[i] * bs; t < (idx[i] + 1) * bs; ++t)",
+     "for (int t = idx[i] * bs; t < (idx[i] + 1) * bs - 1; ++t)", lambda: T_att.test_sparse_equals_masked_dense(0)),
 ]
 
 
