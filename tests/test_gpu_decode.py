@@ -200,3 +200,26 @@ def test_step_replays_as_hip_graph():
         torch.cuda.synchronize()
         for a, b in zip(ref, (p.block_idx, p.n_sel, p.out, p.lse)):
             assert torch.equal(a, b), f"replay {step} differs from the eager step"
+
+
+@pytest.mark.parametrize("splits", [4, 8])
+def test_fused_step_over_several_rounds(splits):
+    """More (pair, split) items than resident workgroups: 128 x 8 pairs at 4 and 8 splits are 4096
+    and 8192 items, above the 2048 workgroups of 256 threads that 256 compute units can hold, so the
+    persistent grid takes each pair's splits in a later round.  Bit-exact against the separate
+    calls, twice in a row on one workspace."""
+    w = DecodeWorkload(name="fused_rounds", B=128, Hq=16, Hkv=8, d=64, bs=64, budget=512, seed=33,
+                       L_range=(600, 4000))
+    run = build_and_run(w, num_splits=splits, mode="fused")
+    p = run.plan
+    assert p.num_splits == splits and p.step_status() == 0
+    args = (run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"])
+    fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    p.step(run.q, *args, mode="calls")
+    torch.cuda.synchronize()
+    for n, a, b in zip(("scores", "block_idx", "n_sel", "out", "lse"), fused,
+                       (p.scores, p.block_idx, p.n_sel, p.out, p.lse)):
+        assert torch.equal(a, b), f"{n} differs between the fused and the separate path"
+    p.step(run.q, *args, mode="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(p.out, fused[3]) and torch.equal(p.lse, fused[4]) and p.step_status() == 0
