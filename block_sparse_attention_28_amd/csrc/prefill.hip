@@ -11,11 +11,15 @@
 //
 // Kernels (gfx950):
 //   prefill_pool_project : mean-pool Q and K per block (partial last block:
-//                          mean of its rows), project with Wq / Wk (fp32)
-//   prefill_gate_scores  : S_ij = gate_scale * A_i . C_j, fp32 64x64 LDS tiles,
-//                          lower-triangular tiles only
-//   prefill_select_rows  : one wave per row: exact top-(k_i - 1) of j < i with
-//                          lower-id ties, then the diagonal
+//                          mean of its rows), one wave per (block, tensor),
+//                          then project with Wq / Wk on fp32 MFMA
+//   prefill_gate_select  : S_ij = gate_scale * A_i . C_j for 16 query blocks
+//                          per workgroup on fp32 MFMA, kept in LDS as order
+//                          keys; one wave per row then selects the exact
+//                          top-(k_i - 1) of j < i with lower-id ties, then the
+//                          diagonal (nb up to 2048)
+//   prefill_gate_scores  : beyond 2048 blocks, S through the workspace in fp32
+//   prefill_select_rows    64x64 LDS tiles, and one wave per row selecting
 //   prefill_attention    : 64 query rows per workgroup; each wave takes 32
 //                          rows and one 32-key half of every kept block, MFMA
 //                          v_mfma_f32_16x16x32_bf16.  S^T = K Q^T so that each
@@ -39,6 +43,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPBS = 64;  // prefill block size (query and key blocks)
+constexpr int kPoolBlocks = 16;  // blocks per workgroup of the gate's pooling kernel
 constexpr float kLazyRescale = 8.0f;  // largest log2 weight before the running reference moves
 
 __device__ __forceinline__ int keep_count(int i, int num, int den) {
@@ -52,90 +57,187 @@ __device__ __forceinline__ void unpack8f(const uint4 w, float *f) {
 }
 
 // ---------------------------------------------------------------- gate ----
-// One workgroup per (chunk of PB blocks, head, batch).  Thread (rg, c) owns the
-// 16-byte column chunk c of rows rg, rg + RG, ...  Output A, C: fp32 [B][H][nb][dg].
+// Gate rows A_i = Wq qbar_i and C_j = Wk kbar_j are stored fp32 with a row
+// stride of DGP = dg rounded up to 128 or 256, zeros past dg, so that the score
+// kernels read whole 32-float runs without a tail.
+__host__ __device__ constexpr int gate_row_stride(int dg) { return dg <= 128 ? 128 : 256; }
+
+// One workgroup per (chunk of PB blocks, head, batch).  Pooling: the 2 PB
+// (block, tensor) items go to the 4 waves round-robin; lane (r4, c) of a wave
+// sums rows r4, r4 + 4, ..., r4 + 60 of its item's column chunk c (16 bytes),
+// 16 loads in flight per lane, and the four row phases combine across lanes.
+// Rows past L read as zero (buffer range), and the mean divides by the rows
+// present.  Then the projections run on fp32 MFMA (below).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_t *q, const uint16_t *k, int H,
                                                                    int L, int nb, const uint16_t *wq,
-                                                                   const uint16_t *wk, int dg, float *A, float *Cm) {
-    constexpr int CH = D / 8, RG = 256 / CH, PB = 8, WB = 8;
+                                                                   const uint16_t *wk, int dg, int dgp, float *A,
+                                                                   float *Cm) {
+    constexpr int CH = D / 8, PB = kPoolBlocks;
+    constexpr int PH = 64 / CH;           // row phases per wave (4)
+    constexpr int RPL = kPBS / PH;        // rows per lane and item (16)
+    static_assert(D == 128, "one wave covers a 256-byte row in 16 lanes");
     const int blk0 = blockIdx.x * PB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int c = tid % CH, rg = tid / CH;
-    __shared__ float part[2][RG][D];
+    // wave-uniform, so that the Q / K descriptor choice per item stays scalar
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     __shared__ float pooled[2][PB][D];  // [Q/K][block][dim]
     const int64_t head = ((int64_t)b * H + h) * L * D;
+    const uint32_t bytes = (uint32_t)L * D * 2u;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + head, bytes), rk = buffer_rsrc(k + head, bytes);
     const int nblk = nb - blk0 < PB ? nb - blk0 : PB;
-    for (int p = 0; p < nblk; ++p) {
-        const int t0 = (blk0 + p) * kPBS;
-        const int rows = L - t0 < kPBS ? L - t0 : kPBS;
-        float aq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        uint4 wqv[kPBS / RG], wkv[kPBS / RG];
+    const int items = 2 * nblk;
+    const uint32_t lane_off = (uint32_t)((lane / CH) * D + (lane % CH) * 8) * 2u;
+    uint4 cur[RPL];
+    for (int it = wave; it < items; it += 4) {
+        {  // the whole offset in the per-lane part, which is what the range check covers
+            const uint32_t voff = (uint32_t)(blk0 + (it >> 1)) * kPBS * D * 2u + lane_off;
+            const __amdgpu_buffer_rsrc_t r = (it & 1) ? rk : rq;
 #pragma unroll
-        for (int i = 0; i < kPBS / RG; ++i) {
-            const int r = rg + i * RG;
-            const int64_t off = head + (int64_t)(t0 + r) * D + c * 8;
-            wqv[i] = r < rows ? *reinterpret_cast<const uint4 *>(q + off) : make_uint4(0, 0, 0, 0);
-            wkv[i] = r < rows ? *reinterpret_cast<const uint4 *>(k + off) : make_uint4(0, 0, 0, 0);
+            for (int m = 0; m < RPL; ++m) cur[m] = buf_ld16(r, voff + (uint32_t)(m * PH * D * 2), 0);
         }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kPBS / RG; ++i) {
+        for (int m = 0; m < RPL; ++m) {
             float f[8];
-            unpack8f(wqv[i], f);
+            unpack8f(cur[m], f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) aq[e] += f[e];
-            unpack8f(wkv[i], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ak[e] += f[e];
+            for (int e = 0; e < 8; ++e) acc[e] += f[e];
         }
+        const int t0 = (blk0 + (it >> 1)) * kPBS;
+        const float inv_rows = 1.0f / (float)(L - t0 < kPBS ? L - t0 : kPBS);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            part[0][rg][c * 8 + e] = aq[e];
-            part[1][rg][c * 8 + e] = ak[e];
-        }
-        __syncthreads();
-        if (tid < 2 * D) {
-            const int which = tid / D, e = tid % D;
-            float s = 0.f;
+        for (int e = 0; e < 8; ++e) acc[e] = sum_xor32(sum_xor16(acc[e]));
+        if (lane < CH) {
 #pragma unroll
-            for (int r = 0; r < RG; ++r) s += part[which][r][e];
-            pooled[which][p][e] = s / (float)rows;
+            for (int e = 0; e < 8; ++e) pooled[it & 1][it >> 1][lane * 8 + e] = acc[e] * inv_rows;
         }
-        __syncthreads();
     }
-    // A[p][r] = Wq[h][r] . qbar_p ; C[p][r] = Wk[h][r] . kbar_p
-    const uint16_t *wqh = wq + (int64_t)h * dg * D + c * 8;
-    const uint16_t *wkh = wk + (int64_t)h * dg * D + c * 8;
-    float *Ah = A + (((int64_t)b * H + h) * nb + blk0) * dg;
-    float *Ch = Cm + (((int64_t)b * H + h) * nb + blk0) * dg;
-    for (int r0 = 0; r0 < dg; r0 += WB * RG) {
-        uint4 w1[WB], w2[WB];
+    __syncthreads();
+    // A[p][r] = Wq[h][r] . qbar_p ; C[p][r] = Wk[h][r] . kbar_p ; zero for dg <= r < dgp.
+    // v_mfma_f32_16x16x4f32 with W rows as M (16-row tiles), the PB pooled blocks
+    // as N (columns PB..15 zero) and the D terms split into four contiguous
+    // quarters, one per k slot (slot kq carries term kq D/4 + s at step s).  Wave
+    // w projects tensor w & 1, row tiles (w >> 1) + 2 m.
+    constexpr int QK = D / 4;
+    const int n = lane & 15, kq = lane >> 4, t = wave & 1;
+    float bop[QK];
 #pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            const int r = r0 + rg + i * RG;
-            w1[i] = r < dg ? *reinterpret_cast<const uint4 *>(wqh + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
-            w2[i] = r < dg ? *reinterpret_cast<const uint4 *>(wkh + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
-        }
+    for (int s4 = 0; s4 < QK; s4 += 4) {
+        const float4 x = n < nblk ? *reinterpret_cast<const float4 *>(&pooled[t][n][kq * QK + s4])
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        bop[s4] = x.x; bop[s4 + 1] = x.y; bop[s4 + 2] = x.z; bop[s4 + 3] = x.w;
+    }
+    const uint16_t *w = (t ? wk : wq) + (int64_t)h * dg * D + kq * QK;
+    // Results go through LDS, 128 columns at a time, so that the chunk's rows
+    // (contiguous in A / C) are written with coalesced 16-byte stores.
+    __shared__ __align__(16) float stage[2][PB][128];
+    for (int c0 = 0; c0 < dgp; c0 += 128) {
+        for (int rt = c0 / 16 + (wave >> 1); rt < c0 / 16 + 8; rt += 2) {
+            const int r = rt * 16 + n;
+            uint4 wv[QK / 8];
 #pragma unroll
-        for (int i = 0; i < WB; ++i) {
-            const int r = r0 + rg + i * RG;
-            float f1[8], f2[8];
-            unpack8f(w1[i], f1);
-            unpack8f(w2[i], f2);
-            for (int p = 0; p < nblk; ++p) {
-                float sa = 0.f, sc = 0.f;
+            for (int v = 0; v < QK / 8; ++v)
+                wv[v] = r < dg ? *reinterpret_cast<const uint4 *>(w + (int64_t)r * D + 8 * v) : make_uint4(0, 0, 0, 0);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sa = fmaf(f1[e], pooled[0][p][c * 8 + e], sa);
-                    sc = fmaf(f2[e], pooled[1][p][c * 8 + e], sc);
-                }
-                sa = group_sum<CH>(sa);
-                sc = group_sum<CH>(sc);
-                if (c == 0 && r < dg) {
-                    Ah[(int64_t)p * dg + r] = sa;
-                    Ch[(int64_t)p * dg + r] = sc;
-                }
+            for (int v = 0; v < QK / 8; ++v) {
+                float f[8];
+                unpack8f(wv[v], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], bop[8 * v + e], acc, 0, 0, 0);
             }
+            // rows rt*16 + 4 kq .. + 3 of block n
+            *reinterpret_cast<float4 *>(&stage[t][n][rt * 16 - c0 + 4 * kq]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
+        __syncthreads();
+        for (int x = tid; x < 2 * nblk * 32; x += 256) {  // 32 float4 per block row of the chunk
+            const int tt = x / (nblk * 32), p = (x / 32) % nblk, q4 = x % 32;
+            float *dst = (tt ? Cm : A) + (((int64_t)b * H + h) * nb + blk0 + p) * dgp + c0 + 4 * q4;
+            *reinterpret_cast<float4 *>(dst) = *reinterpret_cast<const float4 *>(&stage[tt][p][4 * q4]);
+        }
+        __syncthreads();  // the stage is free for the next chunk
+    }
+}
+
+// Scores and selection of 16 query blocks i0 .. i0 + 15 of one (b, h) per
+// workgroup, for nb <= kGsMaxCols.  The 16 x 16 score tiles of key blocks
+// 16 t .. 16 t + 15, t <= the group's own tile, go to the waves round-robin and
+// run on v_mfma_f32_16x16x4f32 (A operand: lane (kq, n) holds row n, k slot kq;
+// B: k slot kq, column n; result: rows 4 kq + e, column n).  The dot product
+// over DGP terms is split into four contiguous quarters, one per k slot: at
+// step s, slot kq carries term kq DGP / 4 + s, so each lane reads its row's and
+// its column's quarter as 16-byte loads straight from the gate rows.  Scores,
+// times gate_scale, are kept in LDS as order keys; then wave w selects rows
+// w, w + 4, w + 8, w + 12 (exact top-(k_i - 1) of j < i, lower id on ties,
+// ascending, then the diagonal i).  The heaviest row groups (the last) start first.
+constexpr int kGsRows = 16;
+constexpr int kGsMaxCols = 2048;
+
+__host__ __device__ constexpr int gs_key_stride(int nb) { return (nb + 15) / 16 * 16 + 4; }
+
+template <int DGP>
+__global__ __launch_bounds__(256) void prefill_gate_select_kernel(const float *A, const float *Cm, int BH, int nb,
+                                                                  float gate_scale, int keep_num, int keep_den,
+                                                                  int kmax_row, int32_t *kv_blocks,
+                                                                  int32_t *kv_count) {
+    constexpr int QK = DGP / 4;        // terms per k slot
+    constexpr int NV = QK / 4;         // 16-byte loads per lane and operand
+    extern __shared__ uint32_t gs_lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nrg = (nb + kGsRows - 1) / kGsRows;
+    const int rgi = nrg - 1 - (int)(blockIdx.x / BH), bh = (int)(blockIdx.x % BH);
+    const int i0 = rgi * kGsRows;
+    const int ks = gs_key_stride(nb);
+    uint32_t *keys = gs_lds;                                   // [16][ks]
+    int *hist = reinterpret_cast<int *>(gs_lds + kGsRows * ks) + wave * 256;
+    const int n = lane & 15, kq = lane >> 4;
+    const float *Ab = A + (int64_t)bh * nb * DGP, *Cb = Cm + (int64_t)bh * nb * DGP;
+    // this lane's query row (clamped: rows past nb are never selected for)
+    const int ia = i0 + n < nb ? i0 + n : nb - 1;
+    float4 av[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) av[v] = *reinterpret_cast<const float4 *>(Ab + (int64_t)ia * DGP + kq * QK + 4 * v);
+    const int ntile = rgi + 1;  // key tiles 0 .. rgi
+    float4 cv[NV], cn[NV];
+    auto load_c = [&](float4 (&buf)[NV], int t) {
+        const int j = 16 * t + n < nb ? 16 * t + n : nb - 1;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) buf[v] = *reinterpret_cast<const float4 *>(Cb + (int64_t)j * DGP + kq * QK + 4 * v);
+    };
+    load_c(cv, wave < ntile ? wave : 0);
+    for (int t = wave; t < ntile; t += 4) {
+        load_c(cn, t + 4 < ntile ? t + 4 : t);  // unconditional (a cached re-read at the end): see the pooling loop
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[v].x, cv[v].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[v].y, cv[v].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[v].z, cv[v].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[v].w, cv[v].w, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) keys[(4 * kq + e) * ks + 16 * t + n] = order_key(acc[e] * gate_scale);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cv[v] = cn[v];
+    }
+    __syncthreads();
+    for (int rr = wave; rr < kGsRows; rr += 4) {
+        const int i = i0 + rr;
+        if (i >= nb) break;
+        const int64_t row = (int64_t)bh * nb + i;
+        int32_t *out = kv_blocks + row * kmax_row;
+        int ki = keep_count(i, keep_num, keep_den);
+        ki = ki > kmax_row ? kmax_row : ki;
+        const int need = ki - 1;
+        if (need > 0 && need < i) {
+            wave_topk_from_keys<LaunchMem>(i, need, keys + rr * ks, hist, out, lane);
+        } else if (need > 0) {  // every earlier block is kept
+            for (int m = lane; m < need; m += 64) out[m] = m;
+        }
+        for (int m = need + lane; m < kmax_row; m += 64) out[m] = m == need ? i : -1;
+        if (lane == 0) kv_count[row] = need + 1;
+        wave_lds_sync();  // the next row's passes reuse hist
     }
 }
 
@@ -600,7 +702,10 @@ extern "C" size_t seer_block_sparse_prefill_workspace_size(int B, int H, int L, 
     if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block_size <= 0 || dg <= 0) return 0;
     const size_t nb = (size_t)(L + block_size - 1) / block_size;
     const size_t bh = (size_t)B * H;
-    return (2 * bh * nb * dg + bh * nb * nb) * sizeof(float);
+    // gate rows A and C; the score matrix only where the fused gate kernel's
+    // LDS cannot hold 16 rows of keys
+    const size_t scores = nb > (size_t)kGsMaxCols ? bh * nb * nb : 0;
+    return (2 * bh * nb * gate_row_stride(dg) + scores) * sizeof(float);
 }
 
 extern "C" int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k, const seer_bf16 *v, int B, int H,
@@ -624,23 +729,37 @@ extern "C" int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k,
         if (nb > 16384 - 256) return SEER_ERR_UNSUPPORTED;
         const size_t need = seer_block_sparse_prefill_workspace_size(B, H, L, d, kPBS, dg);
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SEER_ERR_WORKSPACE;
+        const int dgp = gate_row_stride(dg);
         float *A = static_cast<float *>(workspace);
-        float *Cm = A + (size_t)B * H * nb * dg;
-        float *S = Cm + (size_t)B * H * nb * dg;
-        prefill_pool_project_kernel<128><<<dim3((nb + 7) / 8, H, B), 256, 0, stream>>>(q, k, H, L, nb, wq, wk, dg, A,
-                                                                                       Cm);
+        float *Cm = A + (size_t)B * H * nb * dgp;
+        const dim3 pool_grid((nb + kPoolBlocks - 1) / kPoolBlocks, H, B);
+        prefill_pool_project_kernel<128><<<pool_grid, 256, 0, stream>>>(q, k, H, L, nb, wq, wk, dg, dgp, A, Cm);
         int st = launch_status();
         if (st != SEER_OK) return st;
-        const int nt = (nb + 63) / 64;
-        prefill_gate_scores_kernel<<<dim3(nt, nt, B * H), 256, 0, stream>>>(A, Cm, nb, dg, gate_scale, S);
-        if ((st = launch_status()) != SEER_OK) return st;
-        const int slice = nb + 256;
-        int waves = (int)(65536 / ((size_t)slice * 4));
-        waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
-        prefill_select_rows_kernel<<<dim3((unsigned)((rows + waves - 1) / waves)), 64 * waves,
-                                     (size_t)waves * slice * sizeof(uint32_t), stream>>>(
-            S, B * H, nb, slice, keep_num, keep_den, kmax_row, kv_blocks, kv_count);
-        if ((st = launch_status()) != SEER_OK) return st;
+        if (nb <= kGsMaxCols) {
+            const int nrg = (nb + kGsRows - 1) / kGsRows;
+            const size_t lds = ((size_t)kGsRows * gs_key_stride(nb) + 4 * 256) * sizeof(uint32_t);
+            auto kernel = dgp == 128 ? prefill_gate_select_kernel<128> : prefill_gate_select_kernel<256>;
+            if (lds > 65536 &&
+                hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+                    hipSuccess)
+                return SEER_ERR_LAUNCH;
+            kernel<<<dim3((unsigned)(nrg * B * H)), 256, lds, stream>>>(A, Cm, B * H, nb, gate_scale, keep_num,
+                                                                         keep_den, kmax_row, kv_blocks, kv_count);
+            if ((st = launch_status()) != SEER_OK) return st;
+        } else {
+            float *S = Cm + (size_t)B * H * nb * dgp;
+            const int nt = (nb + 63) / 64;
+            prefill_gate_scores_kernel<<<dim3(nt, nt, B * H), 256, 0, stream>>>(A, Cm, nb, dgp, gate_scale, S);
+            if ((st = launch_status()) != SEER_OK) return st;
+            const int slice = nb + 256;
+            int waves = (int)(65536 / ((size_t)slice * 4));
+            waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+            prefill_select_rows_kernel<<<dim3((unsigned)((rows + waves - 1) / waves)), 64 * waves,
+                                         (size_t)waves * slice * sizeof(uint32_t), stream>>>(
+                S, B * H, nb, slice, keep_num, keep_den, kmax_row, kv_blocks, kv_count);
+            if ((st = launch_status()) != SEER_OK) return st;
+        }
     }
     prefill_attention_kernel<128><<<dim3((unsigned)rows), 256, 0, stream>>>(
         q, k, v, H, L, nb, kv_blocks, kv_count, kmax_row, softmax_scale * kLog2e, out, lse, nullptr);

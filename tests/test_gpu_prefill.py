@@ -97,6 +97,7 @@ SMALL = [
     PrefillWorkload(name="p64_single", B=1, H=1, L=64, d=128, bs=64, keep_num=1, keep_den=10, seed=45),
     PrefillWorkload(name="p5_tiny", B=1, H=1, L=5, d=128, bs=64, keep_num=1, keep_den=10, seed=46),
     PrefillWorkload(name="p1536_dg64", B=1, H=2, L=1536, d=128, bs=64, keep_num=1, keep_den=5, seed=47, dg=64),
+    PrefillWorkload(name="p1300_dg192", B=1, H=2, L=1300, d=128, bs=64, keep_num=1, keep_den=6, seed=52, dg=192),
 ]
 
 
@@ -148,6 +149,24 @@ def test_prefill_full_size_sampled():
     for h in heads:
         say(f"  oracle head {h}")
         check_head(w, x, blocks, counts, out, lse, 0, h, ranges)
+
+
+LONG = [
+    PrefillWorkload(name="p70k_large_lds", B=1, H=1, L=1100 * 64 + 10, d=128, bs=64, keep_num=1, keep_den=10,
+                    seed=50),
+    PrefillWorkload(name="p134k_gate_via_workspace", B=1, H=1, L=2100 * 64, d=128, bs=64, keep_num=1,
+                    keep_den=10, seed=51),
+]
+
+
+@pytest.mark.parametrize("w", LONG, ids=[w.name for w in LONG])
+def test_prefill_long_gate_paths(w):
+    """1101 blocks (16 rows of score keys need more than 64 KiB of LDS) and 2100 blocks (beyond the
+    fused gate kernel: scores through the workspace, then per-row selection): the whole gate against
+    the oracle, the attention on sampled query rows."""
+    x, blocks, counts, out, lse = run(w)
+    L = w.L
+    check_head(w, x, blocks, counts, out, lse, 0, 0, [(0, 64), (L // 2 - 32, L // 2 + 32), (L - 64, L)])
 
 
 # ---- block-level ground truth of prefill attention ----
