@@ -160,6 +160,76 @@ __global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_
     }
 }
 
+// The k largest of the n keys of one row in LDS (0 < k < n), ids ascending to
+// out, by one wave: the same rule and steps as wave_topk_from_keys (8-bit radix
+// passes from the top digit over a 256-bin LDS histogram, then one sweep in id
+// order), with the first 64 KR keys held in registers through all passes, so a
+// pass issues its histogram atomics back to back instead of after a key read each.
+template <int KR>
+__device__ __forceinline__ void wave_topk_row(int n, int k, const uint32_t *keys, int *hist, int32_t *out, int lane) {
+    uint32_t kreg[KR];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) kreg[r] = lane + 64 * r < n ? keys[lane + 64 * r] : 0u;
+    uint32_t prefix = 0;
+    int need = k;  // keys still to take among those matching `prefix`
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hist[lane * 4 + i] = 0;
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+            if (lane + 64 * r < n && (kreg[r] & hi_mask) == prefix) atomicAdd(&hist[(kreg[r] >> shift) & 255u], 1);
+        for (int j = lane + 64 * KR; j < n; j += 64) {
+            const uint32_t key = keys[j];
+            if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        wave_lds_sync();
+        // lane l covers digits 255 - 4l .. 252 - 4l, in descending order
+        int cnt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - 4 * lane - i];
+        const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+        const int incl = wave_inclusive_scan(local, lane);
+        const int excl = incl - local;
+        int digit = 0, rest = 0, cum = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (cum < need && cum + cnt[i] >= need) {  // the digit where the count reaches need
+                digit = 255 - 4 * lane - i;
+                rest = need - cum;
+            }
+            cum += cnt[i];
+        }
+        const uint64_t hit = __ballot(excl < need && incl >= need);  // exactly one lane
+        const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+        prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, src) << shift;
+        need = __builtin_amdgcn_readlane(rest, src);
+        wave_lds_sync();  // every lane has read the bins before the next pass clears them
+    }
+    // keep keys > T and the first `need` keys == T, in id order
+    const uint32_t T = prefix;
+    int written = 0, eq_seen = 0;
+    for (int base = 0, r = 0; base < n; base += 64, ++r) {
+        const int j = base + lane;
+        uint32_t key = 0u;
+#pragma unroll
+        for (int rr = 0; rr < KR; ++rr)
+            if (r == rr) key = kreg[rr];
+        if (r >= KR) key = j < n ? keys[j] : 0u;
+        const bool eq = j < n && key == T;
+        const uint64_t eq_mask = __ballot(eq);
+        const bool take = j < n && (key > T || (eq && eq_seen + lanes_below(eq_mask) < need));
+        const uint64_t take_mask = __ballot(take);
+        const int pos = written + lanes_below(take_mask);
+        if (take && pos < k) out[pos] = j;
+        written += __popcll(take_mask);
+        eq_seen += __popcll(eq_mask);
+    }
+}
+
 // Scores and selection of 16 query blocks i0 .. i0 + 15 of one (b, h) per
 // workgroup, for nb <= kGsMaxCols.  The 16 x 16 score tiles of key blocks
 // 16 t .. 16 t + 15, t <= the group's own tile, go to the waves round-robin and
@@ -231,7 +301,7 @@ __global__ __launch_bounds__(256) void prefill_gate_select_kernel(const float *A
         ki = ki > kmax_row ? kmax_row : ki;
         const int need = ki - 1;
         if (need > 0 && need < i) {
-            wave_topk_from_keys<LaunchMem>(i, need, keys + rr * ks, hist, out, lane);
+            wave_topk_row<8>(i, need, keys + rr * ks, hist, out, lane);
         } else if (need > 0) {  // every earlier block is kept
             for (int m = lane; m < need; m += 64) out[m] = m;
         }
