@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0 = skip)")
     ap.add_argument("--cpu-sequences", type=int, default=2)
-    ap.add_argument("--prefill-steps", type=int, default=5, help="block-sparse prefill timing (0 = skip)")
+    ap.add_argument("--prefill-steps", type=int, default=9, help="block-sparse prefill timing: gated and given-block call pairs (0 = skip)")
     ap.add_argument("--mode", default="calls", choices=("gate_select", "calls", "fused"),
                     help="form of the timed step (the others are timed briefly for context)")
     ap.add_argument("--mode-steps", type=int, default=16, help="steps per form in the context timing (0 = skip)")
@@ -475,20 +475,26 @@ def bench_prefill(steps, dev):
         seer.seer_block_sparse_prefill(x["q"], x["k"], x["v"], pw.bs, x["wq"], x["wk"], gs, pw.keep_num,
                                        pw.keep_den, blocks, counts, ss, out, lse, ws, use_given_blocks=given)
 
-    def timed(given):
-        for _ in range(2):
-            call(given)
+    def timed_pair():
+        """Medians of gated and given-block calls, interleaved after a warm-up, so that a
+        clock that is still ramping up weighs on both alike."""
+        for _ in range(3):
+            call(False)
+            call(True)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        got = {False: [], True: []}
         for _ in range(steps):
-            call(given)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / steps
+            for given in (False, True):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call(given)
+                e1.record()
+                torch.cuda.synchronize()
+                got[given].append(e0.elapsed_time(e1) * 1e3)
+        med = lambda v: sorted(v)[len(v) // 2]
+        return med(got[False]), med(got[True])
 
-    us_total = timed(False)
-    us_attn = timed(True)
+    us_total, us_attn = timed_pair()
     # ground truth: dense causal attention plus every (query block, key block) mass
     mass = torch.empty((pw.B, pw.H, nb, nb), dtype=torch.float32, device=dev)
     gt = seer.seer_prefill_block_mass(x["q"], x["k"], x["v"], pw.bs, ss, out, mass, lse, bind=True)
