@@ -23,9 +23,9 @@ def _gpu():
     seer.load()
 
 
-def run(w: PrefillWorkload, given=None):
+def run(w: PrefillWorkload, given=None, x=None):
     say(f"[gpu] prefill {w.name} B={w.B} H={w.H} L={w.L} keep={w.keep_num}/{w.keep_den} given={given is not None}")
-    x = inputs.prefill_inputs(w, "cuda")
+    x = inputs.prefill_inputs(w, "cuda") if x is None else x
     nb = (w.L + w.bs - 1) // w.bs
     kmax = seer.seer_block_sparse_prefill_kmax_row(w.L, w.bs, w.keep_num, w.keep_den)
     if given is None:
@@ -149,6 +149,28 @@ def test_prefill_full_size_sampled():
     for h in heads:
         say(f"  oracle head {h}")
         check_head(w, x, blocks, counts, out, lse, 0, h, ranges)
+
+
+def test_prefill_gate_exact_ties():
+    """Every key block identical (one key row repeated), so all of a row's candidate scores are
+    equal: each row keeps blocks 0 .. k_i - 2 (lower id first) and its diagonal, exactly as the
+    oracle, for the row counts of 640 blocks plus a partial one."""
+    w = PrefillWorkload(name="p_ties", B=1, H=2, L=640 * 64 + 20, d=128, bs=64, keep_num=1, keep_den=7, seed=53)
+    x = inputs.prefill_inputs(w, "cuda")
+    x["k"] = x["k"][:, :, :1].expand_as(x["k"]).contiguous()
+    x, blocks, counts, out, lse = run(w, x=x)
+    nb = blocks.shape[2]
+    gb, gc = blocks.cpu().numpy(), counts.cpu().numpy()
+    for h in range(w.H):
+        S, rb, rc = oracle.prefill_gate(host_bits(x["q"][0, h]), host_bits(x["k"][0, h]), w.bs,
+                                        host_bits(x["wq"][h]), host_bits(x["wk"][h]), 1 / math.sqrt(w.gate_dim),
+                                        w.keep_num, w.keep_den)
+        np.testing.assert_array_equal(gc[0, h], rc)
+        np.testing.assert_array_equal(gb[0, h], rb)
+        for i in (1, 7, nb // 2, nb - 1):
+            n = int(rc[i])
+            assert gb[0, h, i, :n].tolist() == list(range(n - 1)) + [i]
+    check_head(w, x, blocks, counts, out, lse, 0, 1, [(0, 64), (w.L - 84, w.L)], check_gate=False)
 
 
 LONG = [
