@@ -326,8 +326,9 @@ int seer_decode_step_status(const void *workspace, int *status, hipStream_t stre
  *   wq, wk        bf16 [H][dg][d], dense
  *   kv_blocks     int32 [B][H][nb][kmax_row]; kv_count int32 [B][H][nb]
  *   lse           fp32 [B][H][L] or NULL
- *   workspace     >= seer_block_sparse_prefill_workspace_size(...) bytes (fp32
- *                 projected pooled Q and K and the block score matrix)
+ *   workspace     >= seer_block_sparse_prefill_workspace_size(...) bytes: fp32
+ *                 projected pooled Q and K (rows padded to 128 or 256 floats)
+ *                 and, beyond 2048 blocks only, the block score matrix
  * d = 128, block_size = 64, 1 <= dg <= 256; without given blocks,
  * kmax_row >= seer_block_sparse_prefill_kmax_row(L, block_size, keep_num, keep_den)
  * and nb <= 16128.

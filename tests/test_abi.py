@@ -106,6 +106,19 @@ def test_workspace_size_matches_partials(lib):
     assert lib.seer_sparse_decode_workspace_size(16, 32, 8, 128, 51, 128, 1) == 0
 
 
+def test_prefill_workspace_size(lib):
+    """Gate rows A and C of fp32, padded to 128 floats (dg <= 128) or 256; the block score matrix
+    only beyond 2048 blocks, where the scores go through the workspace."""
+    f = lib.seer_block_sparse_prefill_workspace_size
+    nb = 32768 // 64
+    assert f(1, 32, 32768, 128, 64, 128) == 2 * 32 * nb * 128 * 4
+    assert f(1, 32, 32768, 128, 64, 64) == 2 * 32 * nb * 128 * 4
+    assert f(2, 3, 1000, 128, 64, 192) == 2 * 6 * 16 * 256 * 4
+    assert f(1, 1, 2048 * 64, 128, 64, 128) == 2 * 2048 * 128 * 4
+    assert f(1, 1, 2048 * 64 + 1, 128, 64, 128) == (2 * 2049 * 128 + 2049 * 2049) * 4
+    assert f(1, 1, 0, 128, 64, 128) == 0
+
+
 def test_other_calls_reject_bad_arguments(lib):
     # pool: unsupported block size, then a null cache
     assert lib.seer_pool_k_blocks(FAKE, 1 << 20, 1 << 16, 128, 2, 8, 128, 32, 1024, FAKE, FAKE, 3, FAKE, 16, NULL) == -2
