@@ -176,6 +176,8 @@ def test_prefill_gate_exact_ties():
 LONG = [
     PrefillWorkload(name="p70k_large_lds", B=1, H=1, L=1100 * 64 + 10, d=128, bs=64, keep_num=1, keep_den=10,
                     seed=50),
+    PrefillWorkload(name="p131k_largest_lds", B=1, H=1, L=2048 * 64, d=128, bs=64, keep_num=1, keep_den=10,
+                    seed=54),
     PrefillWorkload(name="p134k_gate_via_workspace", B=1, H=1, L=2100 * 64, d=128, bs=64, keep_num=1,
                     keep_den=10, seed=51),
 ]
@@ -183,9 +185,9 @@ LONG = [
 
 @pytest.mark.parametrize("w", LONG, ids=[w.name for w in LONG])
 def test_prefill_long_gate_paths(w):
-    """1101 blocks (16 rows of score keys need more than 64 KiB of LDS) and 2100 blocks (beyond the
-    fused gate kernel: scores through the workspace, then per-row selection): the whole gate against
-    the oracle, the attention on sampled query rows."""
+    """1101 and 2048 blocks (16 rows of score keys need more than 64 KiB of LDS, up to the fused
+    gate kernel's largest, ~132 KiB) and 2100 blocks (beyond it: scores through the workspace, then
+    per-row selection): the whole gate against the oracle, the attention on sampled query rows."""
     x, blocks, counts, out, lse = run(w)
     L = w.L
     check_head(w, x, blocks, counts, out, lse, 0, 0, [(0, 64), (L // 2 - 32, L // 2 + 32), (L - 64, L)])
