@@ -64,11 +64,11 @@ class Layer:
         self.kpool = torch.zeros((w.B, w.Hkv, self.nb_max, w.d), dtype=torch.float32, device=device)
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs, if they
+def measured_traffic(workload_name, record="sparse_decode_traffic.json"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter runs, if they
     were taken on the current kernel sources and this workload; else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "sparse_decode_traffic.json")
+    path = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(path))
         h = hashlib.sha256()
@@ -519,7 +519,8 @@ def bench_prefill(steps, dev):
                              "note": "dense causal attention + a second QK sweep for every block's mean mass"},
             "roofline": {"kernel": "prefill_attention_kernel", "bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(pw.name, "prefill_attention_traffic.json")}}
 
 
 def cpu_baseline(w, lay, base_L, plan, args):
