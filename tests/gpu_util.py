@@ -31,7 +31,7 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 @dataclass
-class GpuRun:
+class DecodeRun:
     w: DecodeWorkload
     cache: dict
     q: torch.Tensor
@@ -41,7 +41,7 @@ class GpuRun:
 
 
 def build_and_run(w: DecodeWorkload, step: int = 0, num_splits: int = 0, out_dtype=torch.bfloat16,
-                  device="cuda", seqlens=None, mode: str = "gate_select") -> GpuRun:
+                  device="cuda", seqlens=None, mode: str = "gate_select") -> DecodeRun:
     say(f"[gpu] workload={w.name} step={step} splits={num_splits} out={out_dtype} mode={mode}")
     cache = inputs.decode_cache(w, device, seqlens=seqlens)
     q = inputs.decode_query(w, step, device)
@@ -54,10 +54,10 @@ def build_and_run(w: DecodeWorkload, step: int = 0, num_splits: int = 0, out_dty
     plan.pool(cache["k"], kpool, ub, uj)
     plan.step(q, cache["k"], cache["v"], cache["seqlens"], kpool, cache["wq"], cache["wk"], mode=mode)
     torch.cuda.synchronize()
-    return GpuRun(w, cache, q, kpool, plan, nb_max)
+    return DecodeRun(w, cache, q, kpool, plan, nb_max)
 
 
-def oracle_sequence(run: GpuRun, b: int) -> dict:
+def oracle_sequence(run: DecodeRun, b: int) -> dict:
     """Oracle decode step for sequence b alone (its own fp64 pooled cache)."""
     w = run.w
     L = int(run.cache["seqlens"][b])
@@ -91,7 +91,7 @@ def selection_matches(gpu_idx: np.ndarray, n: int, ref_idx: np.ndarray, ref_scor
     return "excused" if np.all(np.abs(ref_scores[diff] - sk) <= window) else False
 
 
-def check_sequence(run: GpuRun, b: int, ref: dict, check_pool=True, check_scores=True) -> dict:
+def check_sequence(run: DecodeRun, b: int, ref: dict, check_pool=True, check_scores=True) -> dict:
     """Compare the GPU's pool/scores/selection/output of sequence b with the oracle's."""
     w = run.w
     L = ref["L"]
