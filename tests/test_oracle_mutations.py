@@ -101,6 +101,18 @@ MUTATIONS = [
      T_pipe.test_prefill_partial_last_block_pools_existing_rows),
     ("prefill gate pools Q for the key side", "        pool_block_rows(k, row_stride, L, d, bs, i, kbar);",
      "        pool_block_rows(q, row_stride, L, d, bs, i, kbar);", T_pipe.test_prefill_partial_last_block_pools_existing_rows),
+    ("prefill gate projections transposed",
+     "sa += so_bf16_to_f64(wq[(int64_t)r * d + e]) * qbar[e];\n                sc += so_bf16_to_f64(wk[(int64_t)r * d + e]) * kbar[e];",
+     "sa += so_bf16_to_f64(wq[(int64_t)e * dg + r]) * qbar[e];\n                sc += so_bf16_to_f64(wk[(int64_t)e * dg + r]) * kbar[e];",
+     T_pipe.test_prefill_gate_single_entry_projections_closed_form),
+    ("prefill gate Wq and Wk swapped",
+     "sa += so_bf16_to_f64(wq[(int64_t)r * d + e]) * qbar[e];\n                sc += so_bf16_to_f64(wk[(int64_t)r * d + e]) * kbar[e];",
+     "sa += so_bf16_to_f64(wk[(int64_t)r * d + e]) * qbar[e];\n                sc += so_bf16_to_f64(wq[(int64_t)r * d + e]) * kbar[e];",
+     T_pipe.test_prefill_gate_single_entry_projections_closed_form),
+    ("prefill gate key projection uses the query's pooled vector",
+     "sc += so_bf16_to_f64(wk[(int64_t)r * d + e]) * kbar[e];",
+     "sc += so_bf16_to_f64(wk[(int64_t)r * d + e]) * qbar[e];",
+     T_pipe.test_prefill_gate_single_entry_projections_closed_form),
     ("a kept block's last token left out", "for (int t = idx[i] * bs; t < (idx[i] + 1) * bs; ++t)",
      "for (int t = idx[i] * bs; t < (idx[i] + 1) * bs - 1; ++t)", lambda: T_att.test_sparse_equals_masked_dense(0)),
 ]

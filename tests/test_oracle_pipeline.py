@@ -162,6 +162,41 @@ def test_prefill_partial_last_block_pools_existing_rows():
     assert S[2, 1] == 0.0 and S[2, 2] == 0.0
 
 
+def test_prefill_gate_single_entry_projections_closed_form():
+    """Wq = e_r e_a^T, Wk = e_r e_c^T with a != c and dg != d: the gate's projections
+    pick column a of the pooled query and column c of the pooled key, so
+    S_ij = gate_scale * Qbar_i[a] * Kbar_j[c] exactly for j <= i (-inf above the
+    diagonal).  Every block's column a (of Q) and c (of K) is constant, with its own
+    value, so the pooled means are known exactly; the other columns are random, so
+    a transposed projection, swapped Wq / Wk or a wrong row index changes S.  The
+    last block is partial (its mean is over the rows it has)."""
+    bs, d, dg, r, a, c = 16, 64, 24, 17, 5, 41
+    nb = 7
+    L = bs * (nb - 1) + 9
+    g = torch.Generator().manual_seed(23)
+    qf = torch.randn(L, d, generator=g)
+    kf = torch.randn(L, d, generator=g)
+    alpha = torch.tensor([0.75, -1.5, 2.0, 0.5, -0.25, 3.0, 1.25])   # exact in bf16
+    beta = torch.tensor([1.0, -0.5, 0.375, 2.5, -1.75, 0.625, -3.0])
+    for i in range(nb):
+        qf[i * bs:(i + 1) * bs, a] = alpha[i]
+        kf[i * bs:(i + 1) * bs, c] = beta[i]
+    tob = lambda x: x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wq = torch.zeros(dg, d); wq[r, a] = 1.0
+    wk = torch.zeros(dg, d); wk[r, c] = 1.0
+    S, blocks, counts = oracle.prefill_gate(tob(qf), tob(kf), bs, tob(wq), tob(wk), 0.5, 1, 2)
+    expect = np.full((nb, nb), -np.inf)
+    for i in range(nb):
+        for j in range(i + 1):
+            expect[i, j] = 0.5 * float(alpha[i]) * float(beta[j])
+    np.testing.assert_array_equal(S, expect)
+    # the selection follows from the closed form: the diagonal plus the best k_i - 1 of j < i
+    for i in range(nb):
+        k_i = (i + 1 + 1) // 2
+        order = sorted(range(i), key=lambda j: (-expect[i, j], j))[:k_i - 1]
+        assert blocks[i, :counts[i]].tolist() == sorted(order) + [i]
+
+
 def test_prefill_keep_counts_golden():
     rows = [list(map(int, ln.split())) for ln in open(os.path.join(GOLDEN, "prefill_keep_counts.txt"))
             if ln.strip() and not ln.startswith("#")]
