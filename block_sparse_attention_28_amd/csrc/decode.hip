@@ -8,27 +8,12 @@
 // tail is always attended: it holds the current token and has no pooled key
 // to be scored with.
 //
-// gfx950 design.  One workgroup (4 waves) per (split, KV head, sequence).  A
-// split owns a contiguous range of "units" (a kept block, or the tail).  For
-// every unit each wave takes a quarter of the block's tokens:
-//   loads : non-temporal 16-byte buffer loads; the unit's first row is a
-//        scalar offset, each lane's rows a fixed 32-bit offset, and rows past
-//        the cache read as zero (the descriptor's range check).
-//   QK : 8 lanes per key row, each lane a 16-byte chunk per 64 head dims;
-//        v_dot2_f32_bf16 with the bf16 query held in registers, then an
-//        8-lane DPP all-reduce.  The key bytes feed all G query heads.
-//   softmax : log2 domain, the scale folded into one FMA; one running max
-//        per head that is uniform across the wave, so partial sums need no
-//        rescaling when the wave's lane groups are combined, and the
-//        accumulators are rescaled only when some head's maximum moved.
-//   PV : probabilities go through LDS to a second layout, one 16-byte value
-//        chunk per lane (a whole 256-byte row per 16 lanes, fully coalesced),
-//        fp32 FMA into G x 8 accumulators per lane.
-// At the end the wave's lane groups and then the 4 waves are combined, and
-// the split writes (unnormalised o, running max, running sum) per head -- or,
-// with a single split, the final normalised output directly.  A second small
-// kernel merges the splits by log-sum-exp.  The bodies of both kernels are in
-// decode_items.hpp, shared with the fused decode step.
+// The kernel bodies, and the description of their gfx950 mapping (LDS-direct
+// K/V tile loads, both products on v_mfma_f32_16x16x32_bf16 with the group's
+// query heads as the N dimension, log2-domain online softmax, per-split
+// (o, m, l) partials), are in decode_items.hpp, shared with the fused decode
+// step.  This file holds the launches: the split kernel, the log-sum-exp merge
+// of the splits, and the dense ground-truth form with its block masses.
 #include "decode_items.hpp"
 
 namespace seer {
@@ -180,7 +165,7 @@ extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h
     if (k_max > 0 && !block_idx) return SEER_ERR_INVALID_ARG;
     if (out_dtype != SEER_OUT_BF16 && out_dtype != SEER_OUT_F32) return SEER_ERR_INVALID_ARG;
     if (skv_t < d || !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !rows_aligned16(k, skv_t) ||
-        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !(softmax_scale == softmax_scale))
+        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !softmax_scale_ok(softmax_scale))
         return SEER_ERR_INVALID_ARG;
     const int G = Hq / Hkv;
     if ((d != 64 && d != 128) || (block_size != 64 && block_size != 128) || !pow2_group(G) || G > 8)
@@ -229,7 +214,7 @@ extern "C" int seer_decode_block_mass(const seer_bf16 *q, int64_t sq_b, int64_t 
         return SEER_ERR_INVALID_ARG;
     if (out_dtype != SEER_OUT_BF16 && out_dtype != SEER_OUT_F32) return SEER_ERR_INVALID_ARG;
     if (skv_t < d || !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !rows_aligned16(k, skv_t) ||
-        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !(softmax_scale == softmax_scale) ||
+        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !softmax_scale_ok(softmax_scale) ||
         !aligned16(workspace))
         return SEER_ERR_INVALID_ARG;
     const int G = Hq / Hkv;

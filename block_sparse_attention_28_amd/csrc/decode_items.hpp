@@ -152,14 +152,16 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         umask = uid + heads_union_cap(nb_max, G, a.k_max);
         for (int i = tid; i < G * W; i += C::NT) bm[i] = 0u;
         __syncthreads();
+        // ids are clamped below both the complete blocks and the bitmap width nb_max
+        const int id_hi = (nc < nb_max ? nc : nb_max) - 1;
         for (int i = tid; i < G * a.k_max; i += C::NT) {
             const int h = i / a.k_max, r = i % a.k_max;
             const int64_t row = (int64_t)b * a.Hq + g * G + h;
             int n = Mem::ldi(a.n_sel + row);
             n = n < 0 ? 0 : (n > kcap ? kcap : n);
-            if (r < n) {
+            if (r < n && id_hi >= 0) {
                 int id = Mem::ldi(a.block_idx + row * a.k_max + r);
-                id = id < 0 ? 0 : (id >= nc ? nc - 1 : id);
+                id = id < 0 ? 0 : (id > id_hi ? id_hi : id);
                 atomicOr(&bm[h * W + id / 32], 1u << (id % 32));
             }
         }
@@ -283,16 +285,35 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         tok0 = __builtin_amdgcn_readfirstlane(tok0);
         cnt = __builtin_amdgcn_readfirstlane(cnt);
         const uint32_t soff = (uint32_t)tok0 * (uint32_t)a.skv_t * 2u;
+        // The tail unit's rows at or past the context end re-read its last token:
+        // they take no weight, and they are neither read past the cache (the range
+        // check covers only the per-lane offset) nor able to bring a non-finite
+        // value of unused cache rows into the P V product (0 * inf is NaN).
+        uint32_t ko[NDMA], vo[NDMA];
+#pragma unroll
+        for (int q = 0; q < NDMA; ++q) {
+            ko[q] = kof[q];
+            vo[q] = vof[q];
+        }
+        if (cnt < BS) {
+#pragma unroll
+            for (int q = 0; q < NDMA; ++q) {
+                const int over = wt0 + q * RPD + lane / CPR - (cnt - 1);
+                const uint32_t back = over > 0 ? (uint32_t)over * (uint32_t)a.skv_t * 2u : 0u;
+                ko[q] -= back;
+                vo[q] -= back;
+            }
+        }
         // This wave's K and V rows into its LDS tiles (the previous unit's reads of
         // them are complete: their results fed the previous unit's MFMAs).
 #pragma unroll
         for (int q = 0; q < NDMA; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)(kt + q * 1024), 16,
-                                                     (int)kof[q], (int)soff, 0, 2);
+                                                     (int)ko[q], (int)soff, 0, 2);
 #pragma unroll
         for (int q = 0; q < NDMA; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(vt + q * 1024), 16,
-                                                     (int)vof[q], (int)soff, 0, 2);
+                                                     (int)vo[q], (int)soff, 0, 2);
         __builtin_amdgcn_s_waitcnt(vmcnt_wait(NDMA));  // the K rows are in LDS
 
         // S^T tiles: lane (g4, n) gets head n's raw scores of tokens 16t + 4 g4 + i.
@@ -326,7 +347,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmax_fast(mx, s[t][i]);
-        mx = max_xor32(max_xor16(mx)) * a.scale_log2;  // the head's 4 lanes; the scale is positive
+        mx = max_xor32(max_xor16(mx)) * a.scale_log2;  // the head's 4 lanes; the host checks the scale is > 0
         const float m_new = fmax_fast(m_run, mx);
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_ref);

@@ -127,7 +127,7 @@ extern "C" int seer_sparse_decode_heads(const seer_bf16 *q, int64_t sq_b, int64_
     if (k_max > 0 && !block_idx) return SEER_ERR_INVALID_ARG;
     if (out_dtype != SEER_OUT_BF16 && out_dtype != SEER_OUT_F32) return SEER_ERR_INVALID_ARG;
     if (skv_t < d || !rows_aligned16(q, sq_h) || !rows_aligned16(q, sq_b) || !rows_aligned16(k, skv_t) ||
-        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !(softmax_scale == softmax_scale))
+        !rows_aligned16(v, skv_t) || skv_h % 8 || skv_b % 8 || !softmax_scale_ok(softmax_scale))
         return SEER_ERR_INVALID_ARG;
     const int G = Hq / Hkv;
     if ((d != 64 && d != 128) || (block_size != 64 && block_size != 128) || !pow2_group(G) || G > 8 ||

@@ -785,7 +785,7 @@ extern "C" int seer_block_sparse_prefill(const seer_bf16 *q, const seer_bf16 *k,
                                          void *workspace, size_t workspace_bytes, seer_bf16 *out, float *lse,
                                          hipStream_t stream) {
     if (!q || !k || !v || !kv_blocks || !kv_count || !out) return SEER_ERR_INVALID_ARG;
-    if (B <= 0 || H <= 0 || L <= 0 || kmax_row <= 0 || !(softmax_scale == softmax_scale)) return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || L <= 0 || kmax_row <= 0 || !softmax_scale_ok(softmax_scale)) return SEER_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SEER_ERR_INVALID_ARG;
     if (d != 128 || block_size != kPBS) return SEER_ERR_UNSUPPORTED;
     const int nb = (L + kPBS - 1) / kPBS;
@@ -840,7 +840,7 @@ extern "C" int seer_prefill_block_mass(const seer_bf16 *q, const seer_bf16 *k, c
                                        int L, int d, int block_size, float softmax_scale, seer_bf16 *out, float *lse,
                                        float *mass, hipStream_t stream) {
     if (!q || !k || !v || !out || !mass) return SEER_ERR_INVALID_ARG;
-    if (B <= 0 || H <= 0 || L <= 0 || !(softmax_scale == softmax_scale)) return SEER_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || L <= 0 || !softmax_scale_ok(softmax_scale)) return SEER_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SEER_ERR_INVALID_ARG;
     if (d != 128 || block_size != kPBS) return SEER_ERR_UNSUPPORTED;
     const int nb = (L + kPBS - 1) / kPBS;

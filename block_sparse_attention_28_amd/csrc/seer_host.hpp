@@ -23,6 +23,10 @@ inline int launch_status() {
     return e == hipSuccess ? SEER_OK : SEER_ERR_LAUNCH;
 }
 
+// Softmax scales the kernels accept: positive and finite (the running maxima
+// are taken on the raw scores and then scaled, which needs a positive scale).
+inline bool softmax_scale_ok(float s) { return s > 0.f && s < __builtin_inff(); }
+
 inline bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 struct SelectPolicy;

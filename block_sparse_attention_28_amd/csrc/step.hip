@@ -213,7 +213,7 @@ extern "C" int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, 
     if (!q || !k || !v || !seqlens || !wq || !wk || !kpool || !scores || !n_sel || !out || !workspace)
         return SEER_ERR_INVALID_ARG;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || nb_max <= 0 || budget_tokens < 0 || kv_capacity < 0 ||
-        num_splits < 0 || dg < 1 || dg > 256 || !(gate_scale == gate_scale) || !(softmax_scale == softmax_scale))
+        num_splits < 0 || dg < 1 || dg > 256 || !(gate_scale == gate_scale) || !softmax_scale_ok(softmax_scale))
         return SEER_ERR_INVALID_ARG;
     const int k_max = block_size > 0 ? budget_tokens / block_size : 0;
     if (k_max > 0 && !block_idx) return SEER_ERR_INVALID_ARG;

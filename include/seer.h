@@ -196,7 +196,14 @@ int seer_gate_select_ex(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
  *   lse        fp32 [B][Hq] or NULL
  *   workspace  >= seer_sparse_decode_workspace_size(...) bytes of fp32 partial
  *              results (none is needed, size 0, when a single split is used)
- * d in {64, 128}; block_size in {64, 128}; Hq / Hkv in {1, 2, 4, 8}.
+ * d in {64, 128}; block_size in {64, 128}; Hq / Hkv in {1, 2, 4, 8};
+ * softmax_scale > 0 and finite (else SEER_ERR_INVALID_ARG).
+ * Only cache rows t < seqlens[b] are read: rows between the context end and
+ * kv_capacity (which need not be a multiple of block_size) may hold anything,
+ * NaN included.  The K/V rows of one (b, KV head) are addressed with 32-bit
+ * byte offsets: kv_capacity * skv_t * 2 must stay below 2^31, else
+ * SEER_ERR_UNSUPPORTED (the same limit holds for every call below that reads
+ * the K/V cache).
  */
 int seer_sparse_decode_num_splits(int B, int Hkv, int k_max, int block_size, int num_splits);
 size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for n in ("seer_pool_k_blocks", "seer_gate_scores", "seer_select_blocks", "seer_sparse_decode"):
+    for n in ("seer_pool_k_blocks", "seer_gate_scores", "seer_select_blocks", "seer_sparse_decode",
+              "seer_block_sparse_prefill"):
         assert n in names
 
 
@@ -69,6 +70,28 @@ def decode_args(**over):
 ])
 def test_sparse_decode_rejects_bad_arguments(lib, over, status):
     assert lib.seer_sparse_decode(*decode_args(**over)) == status
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, float("inf"), float("nan")])
+def test_decode_calls_reject_a_non_positive_softmax_scale(lib, scale):
+    """The kernels take running maxima on the raw scores and scale them after: only a positive,
+    finite softmax scale is accepted, by every call that runs the decode or prefill attention."""
+    assert lib.seer_sparse_decode(*decode_args(scale=scale)) == -1
+    a = [FAKE, 32 * 128, 128, FAKE, FAKE, 8 * 1024 * 128, 1024 * 128, 128, 1024, FAKE, 2, 32, 8, 128, 64,
+         C.c_float(scale), 16, 0, FAKE, 1 << 30, FAKE, 0, NULL, FAKE, NULL]
+    assert lib.seer_decode_block_mass(*a) == -1
+    h = [FAKE, 32 * 128, 128, FAKE, FAKE, 8 * 1024 * 128, 1024 * 128, 128, 1024, FAKE, FAKE, FAKE, 4, 16, 2, 32, 8,
+         128, 64, C.c_float(scale), 1, NULL, 0, FAKE, 0, NULL, NULL]
+    assert lib.seer_sparse_decode_heads(*h) == -1
+    st = [FAKE, 32 * 128, 128, FAKE, FAKE, 8 * 1024 * 128, 1024 * 128, 128, 1024, FAKE, FAKE, FAKE, 128,
+          C.c_float(0.1), FAKE, 16, 2, 32, 8, 128, 64, 256, C.c_float(scale), 1, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+          FAKE, 0, NULL, NULL]
+    assert lib.seer_decode_step(*st) == -1
+    pf = [FAKE, FAKE, FAKE, 1, 2, 1024, 128, 64, NULL, NULL, 128, C.c_float(0.1), 1, 10, FAKE, FAKE, 4, 1,
+          C.c_float(scale), NULL, 0, FAKE, NULL, NULL]
+    assert lib.seer_block_sparse_prefill(*pf) == -1
+    assert lib.seer_prefill_block_mass(FAKE, FAKE, FAKE, 1, 2, 1024, 128, 64, C.c_float(scale), FAKE, NULL, FAKE,
+                                       NULL) == -1
 
 
 def test_block_mass_rejects_bad_arguments(lib):

@@ -28,10 +28,16 @@ def _gpu():
     seer.load()
 
 
+STEP_FORMS = ["calls", "gate_select", "fused"]
+
+
+@pytest.mark.parametrize("mode", STEP_FORMS)
 @pytest.mark.parametrize("splits", [0, 1, 2, 5])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_tiny_workload_full(splits, out_dtype):
-    run = build_and_run(TINY_DECODE, num_splits=splits, out_dtype=out_dtype)
+def test_tiny_workload_full(splits, out_dtype, mode):
+    """Every form of the step (the three calls, the one-launch gate + select, the fused persistent
+    launch) against the oracle, not only against each other."""
+    run = build_and_run(TINY_DECODE, num_splits=splits, out_dtype=out_dtype, mode=mode)
     ref = oracle_sequence(run, 0)
     st = check_sequence(run, 0, ref)
     if out_dtype == torch.float32:
@@ -39,9 +45,12 @@ def test_tiny_workload_full(splits, out_dtype):
     say(f"  tiny splits={splits} max_err={st['max_err']:.3e}")
 
 
+@pytest.mark.parametrize("mode", STEP_FORMS)
 @pytest.mark.parametrize("w", [DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE], ids=lambda w: w.name)
-def test_full_size_pipeline_sampled(w):
-    run = build_and_run(w)
+def test_full_size_pipeline_sampled(w, mode):
+    """Full-size workloads in the launch configuration the benchmark times, each step form compared
+    with the oracle on sampled sequences."""
+    run = build_and_run(w, mode=mode)
     worst = 0.0
     for b in sample_sequences(w.B, seed=w.seed):
         say(f"  oracle b={b} L={int(run.cache['seqlens'][b])}")

@@ -1,0 +1,175 @@
+"""Cache rows the context does not reach are never read.
+
+A decode reads K/V rows t < seqlens[b] only.  Here the rows between each
+sequence's context end and the cache capacity hold NaN, and the capacity is
+not a multiple of the block size, so the last (b, KV head)'s tail block runs
+past the end of its rows.  Every decode entry point (the three-call step, the
+one-launch gate + select form, the fused step, the dense ground truth and the
+per-head decode) must still match the fp64 oracle, which sees only the
+context rows ("SeerAttention-R: Sparse Attention Adaptation for Long
+Reasoning", abstract: the decoding kernel attends the kept blocks and the
+current, incomplete block)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_28_amd import inputs, pipeline, seer
+from block_sparse_attention_28_amd.workloads import DecodeWorkload
+
+from gpu_util import DecodeRun, OUT_ATOL, check_sequence, host_bits, oracle_sequence, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    seer.load()
+
+
+CASES = [
+    # (name, B, Hq, Hkv, d, bs, budget, context lengths)
+    ("bs64_tails", 3, 8, 2, 128, 64, 256, [130, 64 * 5 + 63, 37]),
+    ("bs128_g4_d64", 2, 8, 2, 64, 128, 384, [128 * 6 + 5, 128 * 3 + 127]),
+    ("g8_no_tail_last", 2, 16, 2, 128, 64, 512, [64 * 9 + 1, 64 * 12]),
+]
+
+
+def nan_padded_cache(w: DecodeWorkload, lens):
+    """K/V with capacity max(L) + 3 rows (not a block multiple), NaN in every row >= L_b."""
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    full = inputs.decode_cache(w, "cuda", seqlens=seqlens)
+    cap = max(lens) + 3
+    assert cap % w.bs != 0
+    c = dict(full)
+    for name in ("k", "v"):
+        t = full[name][:, :, :cap].contiguous()
+        for b, L in enumerate(lens):
+            t[b, :, L:] = float("nan")
+        c[name] = t
+    return c
+
+
+def make_run(w, lens, mode, out_dtype=torch.float32):
+    c = nan_padded_cache(w, lens)
+    q = inputs.decode_query(w, 0, "cuda")
+    nb_max = c["k"].shape[2] // w.bs
+    shape = pipeline.DecodeShape(w.B, w.Hq, w.Hkv, w.d, w.bs, w.budget, nb_max, w.gate_dim)
+    plan = pipeline.DecodePlan(shape, "cuda", out_dtype=out_dtype)
+    kpool = torch.zeros((w.B, w.Hkv, nb_max, w.d), dtype=torch.float32, device="cuda")
+    ub, uj = pipeline.full_pool_lists(c["seqlens"].cpu(), w.bs)
+    plan.pool(c["k"], kpool, ub, uj)
+    plan.step(q, c["k"], c["v"], c["seqlens"], kpool, c["wq"], c["wk"], mode=mode)
+    torch.cuda.synchronize()
+    return DecodeRun(w, c, q, kpool, plan, nb_max)
+
+
+def workload(case):
+    name, B, Hq, Hkv, d, bs, budget, lens = case
+    return DecodeWorkload(name=name, B=B, Hq=Hq, Hkv=Hkv, d=d, bs=bs, budget=budget, seed=40 + len(name)), lens
+
+
+@pytest.mark.parametrize("mode", ["calls", "gate_select", "fused"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_step_ignores_rows_past_the_context(case, mode):
+    w, lens = workload(case)
+    say(f"[gpu] unused rows {w.name} mode={mode} lens={lens}")
+    run = make_run(w, lens, mode)
+    assert torch.isfinite(run.plan.out).all() and not torch.isnan(run.plan.lse).any()
+    for b in range(w.B):
+        st = check_sequence(run, b, oracle_sequence(run, b))
+        assert st["max_err"] < 1e-4, st
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_ground_truth_ignores_rows_past_the_context(case):
+    w, lens = workload(case)
+    say(f"[gpu] unused rows, ground truth {w.name}")
+    c = nan_padded_cache(w, lens)
+    q = inputs.decode_query(w, 0, "cuda")
+    nb_max = c["k"].shape[2] // w.bs
+    mass = torch.empty((w.B, w.Hkv, nb_max + 1), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    wsb = seer.seer_decode_block_mass_workspace_size(w.B, w.Hq, w.Hkv, w.d, nb_max, w.bs, 0)
+    ws = torch.zeros((wsb + 3) // 4, dtype=torch.float32, device="cuda")
+    seer.seer_decode_block_mass(q, c["k"], c["v"], c["seqlens"], w.bs, 1 / math.sqrt(w.d), mass, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(mass).all() and torch.isfinite(out).all()
+    for b, L in enumerate(lens):
+        k, v = host_bits(c["k"][b, :, :L]), host_bits(c["v"][b, :, :L])
+        qb = host_bits(q[b])
+        for g in range(w.Hkv):
+            ro, rl, _ = oracle.sparse_attention(qb[g * w.G:(g + 1) * w.G], k[g], v[g], w.bs,
+                                                np.arange(L // w.bs, dtype=np.int32), 1 / math.sqrt(w.d), L=L)
+            err = np.abs(out[b, g * w.G:(g + 1) * w.G].double().cpu().numpy() - ro).max()
+            assert err < 1e-4, (b, g, err)
+            _, _, ref_mass = oracle.decode_block_mass(qb[g * w.G:(g + 1) * w.G], k[g], v[g], w.bs,
+                                                      1 / math.sqrt(w.d), L=L)
+            nc = L // w.bs
+            gm = mass[b, g].double().cpu().numpy()
+            np.testing.assert_allclose(gm[:nc], ref_mass[:nc], rtol=0, atol=2e-5)
+            if L % w.bs:
+                assert abs(gm[nb_max] - ref_mass[nc]) < 2e-5
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_per_head_decode_ignores_rows_past_the_context(case):
+    w, lens = workload(case)
+    say(f"[gpu] unused rows, per-head {w.name}")
+    c = nan_padded_cache(w, lens)
+    q = inputs.decode_query(w, 0, "cuda")
+    nb_max = c["k"].shape[2] // w.bs
+    kpool = torch.zeros((w.B, w.Hkv, nb_max, w.d), dtype=torch.float32, device="cuda")
+    ub, uj = pipeline.full_pool_lists(c["seqlens"].cpu(), w.bs)
+    seer.seer_pool_k_blocks(c["k"], ub, uj, kpool, w.bs)
+    scores = torch.empty((w.B, w.Hq, nb_max), device="cuda")
+    idx = torch.empty((w.B, w.Hq, w.k_max), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((w.B, w.Hq), dtype=torch.int32, device="cuda")
+    gscale, sscale = 1 / math.sqrt(w.gate_dim), 1 / math.sqrt(w.d)
+    seer.seer_gate_select_heads(q, c["wq"], c["wk"], kpool, c["seqlens"], w.bs, gscale, w.budget, scores, idx, n_sel)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    wsb = seer.seer_sparse_decode_heads_workspace_size(w.B, w.Hq, w.Hkv, w.d, w.k_max, nb_max, w.bs, 0)
+    ws = torch.zeros((wsb + 3) // 4 + 4, dtype=torch.float32, device="cuda")
+    seer.seer_sparse_decode_heads(q, c["k"], c["v"], c["seqlens"], idx, n_sel, nb_max, w.bs, sscale, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    gi, gn = idx.cpu().numpy(), n_sel.cpu().numpy()
+    for b, L in enumerate(lens):
+        k, v = host_bits(c["k"][b, :, :L]), host_bits(c["v"][b, :, :L])
+        qb = host_bits(q[b])
+        for h in range(w.Hq):
+            g = h // w.G
+            ro, _, _ = oracle.sparse_attention(qb[h:h + 1], k[g], v[g], w.bs, gi[b, h, :gn[b, h]], sscale, L=L)
+            err = np.abs(out[b, h].double().cpu().numpy() - ro[0]).max()
+            assert err < 1e-4, (b, h, err)
+
+
+def test_per_head_decode_clamps_ids_beyond_the_table_width():
+    """Block ids at or past nb_max (the pooled-table width that bounds the per-head bitmaps) are
+    clamped to nb_max - 1: wrong blocks by contract, but no access outside the bitmaps.  The result
+    is the attention over the clamped (deduplicated) sets plus the tail."""
+    w = DecodeWorkload(name="ph_clamp", B=1, Hq=4, Hkv=1, d=128, bs=64, budget=192, seed=77)
+    L, nb_max = 64 * 40 + 10, 8   # ids up to 39 would index bitmap word 1 of a 1-word bitmap
+    c = inputs.decode_cache(w, "cuda", seqlens=torch.tensor([L], dtype=torch.int32))
+    q = inputs.decode_query(w, 0, "cuda")
+    ids = torch.tensor([[[3, 15, 39], [1, 2, 7], [7, 8, 100], [0, 5, 6]]], dtype=torch.int32, device="cuda")
+    n_sel = torch.full((1, 4), 3, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 4, w.d), dtype=torch.float32, device="cuda")
+    sscale = 1 / math.sqrt(w.d)
+    wsb = seer.seer_sparse_decode_heads_workspace_size(1, 4, 1, w.d, 3, nb_max, w.bs, 0)
+    ws = torch.zeros((wsb + 3) // 4 + 4, dtype=torch.float32, device="cuda")
+    say(f"[gpu] per-head id clamp L={L} nb_max={nb_max}")
+    seer.seer_sparse_decode_heads(q, c["k"], c["v"], c["seqlens"], ids, n_sel, nb_max, w.bs, sscale, out, None, ws)
+    torch.cuda.synchronize()
+    k, v, qb = host_bits(c["k"][0, 0, :L]), host_bits(c["v"][0, 0, :L]), host_bits(q[0])
+    for h in range(4):
+        kept = sorted({min(int(i), nb_max - 1) for i in ids[0, h].tolist()})
+        ro, _, _ = oracle.sparse_attention(qb[h:h + 1], k, v, w.bs, np.array(kept, dtype=np.int32), sscale, L=L)
+        err = np.abs(out[0, h].double().cpu().numpy() - ro[0]).max()
+        assert err < 1e-4, (h, kept, err)
