@@ -16,6 +16,8 @@
 // of the splits, and the dense ground-truth form with its block masses.
 #include "decode_items.hpp"
 
+#include <mutex>
+
 namespace seer {
 
 template <int D, int BS, int G>
@@ -153,12 +155,43 @@ extern "C" size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int 
     return (size_t)B * Hq * s * ((size_t)d + 2) * sizeof(float);
 }
 
-extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
-                                  const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t, int kv_capacity,
-                                  const int32_t *seqlens, const int32_t *block_idx, const int32_t *n_sel, int k_max,
-                                  int B, int Hq, int Hkv, int d, int block_size, float softmax_scale, int num_splits,
-                                  void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
-                                  hipStream_t stream) {
+// ------------------------------------------------- allocation-free form ----
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the split partials live in
+// this file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SEER_NOALLOC_SCRATCH_BYTES];
+
+namespace seer {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, or null if the lookup failed.
+static void *scratch_device_ptr() {
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices] = {nullptr};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
+// Validation and launch shared by seer_sparse_decode and its allocation-free form;
+// `partials` (a caller workspace, or the static scratch) holds `ws_bytes` bytes.
+static int sparse_decode_impl(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
+                              const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t, int kv_capacity,
+                              const int32_t *seqlens, const int32_t *block_idx, const int32_t *n_sel, int k_max,
+                              int B, int Hq, int Hkv, int d, int block_size, float softmax_scale, int num_splits,
+                              void *workspace, size_t workspace_bytes, bool static_scratch, void *out,
+                              int out_dtype, float *lse, hipStream_t stream) {
     if (!q || !k || !v || !seqlens || !n_sel || !out) return SEER_ERR_INVALID_ARG;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || k_max < 0 || kv_capacity < 0 || num_splits < 0)
         return SEER_ERR_INVALID_ARG;
@@ -172,6 +205,14 @@ extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h
         return SEER_ERR_UNSUPPORTED;
     const int S = seer_sparse_decode_num_splits(B, Hkv, k_max, block_size, num_splits);
     const size_t need = seer_sparse_decode_workspace_size(B, Hq, Hkv, d, k_max, block_size, S);
+    if (static_scratch) {
+        if (need > SEER_NOALLOC_SCRATCH_BYTES) return SEER_ERR_WORKSPACE;
+        if (need > 0) {
+            workspace = scratch_device_ptr();
+            if (!workspace) return SEER_ERR_LAUNCH;
+            workspace_bytes = SEER_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SEER_ERR_WORKSPACE;
     if (S > kMaxSplits) return SEER_ERR_INVALID_ARG;
     if ((int64_t)kv_capacity * skv_t * 2 > 0x7fffffffLL) return SEER_ERR_UNSUPPORTED;  // buffer offsets are 32-bit
@@ -189,6 +230,30 @@ extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h
     a.blk_lse = nullptr; a.units_max = 0;
     if (d == 128) return block_size == 128 ? dispatch_group<128, 128>(a, B, G, stream) : dispatch_group<128, 64>(a, B, G, stream);
     return block_size == 128 ? dispatch_group<64, 128>(a, B, G, stream) : dispatch_group<64, 64>(a, B, G, stream);
+}
+
+}  // namespace seer
+
+extern "C" int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
+                                  const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t, int kv_capacity,
+                                  const int32_t *seqlens, const int32_t *block_idx, const int32_t *n_sel, int k_max,
+                                  int B, int Hq, int Hkv, int d, int block_size, float softmax_scale, int num_splits,
+                                  void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                                  hipStream_t stream) {
+    return sparse_decode_impl(q, sq_b, sq_h, k, v, skv_b, skv_h, skv_t, kv_capacity, seqlens, block_idx, n_sel,
+                              k_max, B, Hq, Hkv, d, block_size, softmax_scale, num_splits, workspace,
+                              workspace_bytes, false, out, out_dtype, lse, stream);
+}
+
+extern "C" int seer_sparse_decode_noalloc(const seer_bf16 *q, int64_t sq_b, int64_t sq_h, const seer_bf16 *k,
+                                          const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                                          int kv_capacity, const int32_t *seqlens, const int32_t *block_idx,
+                                          const int32_t *n_sel, int k_max, int B, int Hq, int Hkv, int d,
+                                          int block_size, float softmax_scale, int num_splits, void *out,
+                                          int out_dtype, float *lse, hipStream_t stream) {
+    return sparse_decode_impl(q, sq_b, sq_h, k, v, skv_b, skv_h, skv_t, kv_capacity, seqlens, block_idx, n_sel,
+                              k_max, B, Hq, Hkv, d, block_size, softmax_scale, num_splits, nullptr, 0, true, out,
+                              out_dtype, lse, stream);
 }
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }

@@ -51,6 +51,8 @@ SIGNATURES = {
     "seer_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _F, _I, _P, _SZ, _P, _I, _P, _P]),
+    "seer_sparse_decode_noalloc": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _I, _I, _I,
+                                        _I, _I, _F, _I, _P, _I, _P, _P]),
     "seer_gate_select_heads": (_I, [_P, _I64, _I64, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
                                     _P]),
     "seer_sparse_decode_heads_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
@@ -268,6 +270,22 @@ def seer_sparse_decode(q, k, v, seqlens, block_idx, n_sel, block_size: int, soft
         k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq, Hkv, d,
         block_size, float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), out_dtype,
         _ptr(lse), _stream(stream), bind=bind)
+
+
+def seer_sparse_decode_noalloc(q, k, v, seqlens, block_idx, n_sel, block_size: int, softmax_scale: float, out,
+                               lse=None, num_splits: int = 0, stream=None, bind: bool = False):
+    """seer_sparse_decode with its split partials in the library's static device scratch (no workspace)."""
+    _bits(q), _bits(k), _bits(v)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    assert k.stride() == v.stride() and out.is_contiguous()
+    k_max = block_idx.shape[2] if block_idx is not None else 0
+    out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
+    return _call(
+        "seer_sparse_decode_noalloc", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0),
+        k.stride(1), k.stride(2), cap, _ptr(seqlens), _ptr(block_idx) if k_max else None, _ptr(n_sel), k_max, B, Hq,
+        Hkv, d, block_size, float(softmax_scale), int(num_splits), _ptr(out), out_dtype, _ptr(lse), _stream(stream),
+        bind=bind)
 
 
 def seer_gate_select_heads(q, wq, wk, kpool, seqlens, block_size: int, gate_scale: float, budget_tokens: int,

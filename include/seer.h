@@ -216,6 +216,29 @@ int seer_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                        void *out, int out_dtype, float *lse, hipStream_t stream);
 
 /*
+ * seer_sparse_decode without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and checks as
+ * seer_sparse_decode (bit for bit), except that the split partials go to a
+ * static device array of SEER_NOALLOC_SCRATCH_BYTES inside the library: each
+ * GPU the library runs on holds one such array from the first call on it
+ * until the process ends.  The call allocates nothing.  A shape whose
+ * partials need more than the array (seer_sparse_decode_workspace_size with
+ * the same arguments) returns SEER_ERR_WORKSPACE; a failed lookup of the
+ * array's device address returns SEER_ERR_LAUNCH.  Every call on a GPU shares
+ * that GPU's array: calls that may overlap on one GPU (on different streams,
+ * or from several threads without ordering) race and give wrong results; order
+ * them on one stream.
+ */
+#define SEER_NOALLOC_SCRATCH_BYTES (8u << 20)
+int seer_sparse_decode_noalloc(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                               const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                               int kv_capacity, const int32_t *seqlens, const int32_t *block_idx,
+                               const int32_t *n_sel, int k_max, int B, int Hq, int Hkv, int d, int block_size,
+                               float softmax_scale, int num_splits, void *out, int out_dtype, float *lse,
+                               hipStream_t stream);
+
+/*
  * Per-query-head selection (the alternative GQA reading): every query head h
  * keeps its own k = min(budget / bs, nc_b) blocks by its own gate score
  * s_hj = gate_scale * (Wq[g] q_h) . (Wk[g] kp_j) (no group mean) and attends

@@ -167,3 +167,14 @@ def test_other_calls_reject_bad_arguments(lib):
     assert lib.seer_gate_select(*gs) == -1
     gs[17], gs[12], gs[1], gs[2] = FAKE, 96, 32 * 96, 96
     assert lib.seer_gate_select(*gs) == -2
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_scratch(lib):
+    """The allocation-free decode refuses, before any launch, a shape whose split partials exceed
+    its static scratch (8 MiB): B 64, 64 query heads, 16 splits, d 128 need 64*64*16*130*4 bytes."""
+    args = decode_args(B=64, Hq=64, Hkv=8, splits=16)
+    del args[20:22]                     # no workspace arguments
+    assert lib.seer_sparse_decode_noalloc(*args) == -3
+    args = decode_args(B=2, Hq=32, Hkv=8, splits=4, scale=-1.0)
+    del args[20:22]
+    assert lib.seer_sparse_decode_noalloc(*args) == -1
