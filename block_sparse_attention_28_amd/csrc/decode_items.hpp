@@ -199,9 +199,17 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         nsel = GT ? kcap : (KL ? kept_n : Mem::ldi(a.n_sel + b * a.Hkv + g));
         nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
     }
+    // Each unit is NW slices, one per wave (wave w always takes the unit's
+    // w-th quarter of tokens).  The S splits divide the pair's slices evenly, so
+    // every split moves the same bytes to within one slice even when the units
+    // do not divide by S; a unit at a split boundary is shared by two splits.
     const int units = nsel + (tail > 0 ? 1 : 0);
-    const int u0 = (int)(((int64_t)split * units) / a.num_splits);
-    const int u1 = (int)(((int64_t)(split + 1) * units) / a.num_splits);
+    const int64_t nslices = (int64_t)units * C::NW;
+    const int i0 = (int)((split * nslices) / a.num_splits);  // this split's slices [i0, i1)
+    const int i1 = (int)(((split + 1) * nslices) / a.num_splits);
+    // This wave's units: those whose slice u NW + wave lies in [i0, i1).
+    const int u0 = __builtin_amdgcn_readfirstlane((i0 - wave + C::NW - 1) / C::NW);
+    const int u1 = __builtin_amdgcn_readfirstlane((i1 - wave + C::NW - 1) / C::NW);
 
     constexpr int TPW = C::TPW;   // tokens per wave per unit: 32 or 16
     constexpr int NKT = TPW / 16;  // 16-token tiles per wave
@@ -213,7 +221,6 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     constexpr int XM = CPR / 2 - 1;  // 32-byte chunk swizzle mask
     static_assert(G <= 16 && (TPW == 16 || TPW == 32), "MFMA decode tile");
     const int g4 = lane >> 4, n = lane & 15;
-    const int wt0 = wave * TPW;  // first token of this wave inside a unit
 
     // Q operand: lane (g4, n) holds dims 8 g4 + 32 ks .. + 7 of head n (zero for n >= G).
     bf16x8_t qop[KS];
@@ -222,7 +229,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     for (int ks = 0; ks < KS; ++ks)
         qop[ks] = __builtin_bit_cast(bf16x8_t, n < G ? ldg16(qb + n * a.sq_h + 8 * g4 + 32 * ks) : make_uint4(0, 0, 0, 0));
 
-    // K/V of (b, g) through buffer descriptors: a unit's first row is a scalar
+    // K/V of (b, g) through buffer descriptors: a slice's first row is a scalar
     // byte offset, each lane's rows and chunks a fixed 32-bit offset.
     const uint16_t *kb = a.k + b * a.skv_b + g * a.skv_h;
     const uint16_t *vb = a.v + b * a.skv_b + g * a.skv_h;
@@ -239,8 +246,8 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         const int rr = q * RPD + lane / CPR, s = lane % CPR;
         const int kc = s ^ (rr & (CPR - 1));
         const int vc = ((((s >> 1) ^ (rr & XM)) << 1) | (s & 1));
-        kof[q] = (uint32_t)(((wt0 + rr) * a.skv_t + kc * 8) * 2);
-        vof[q] = (uint32_t)(((wt0 + rr) * a.skv_t + vc * 8) * 2);
+        kof[q] = (uint32_t)((rr * a.skv_t + kc * 8) * 2);
+        vof[q] = (uint32_t)((rr * a.skv_t + vc * 8) * 2);
     }
     char *const kt = reinterpret_cast<char *>(sm.kt[wave]);
     char *const vt = reinterpret_cast<char *>(sm.vt[wave]);
@@ -256,8 +263,9 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_part = 0.f;  // of head n
 
-    int ids = 0, id0 = u0 - 64;  // kept block ids of units [id0, id0 + 64), one per lane
+    int ids = 0, id0 = -(1 << 30);  // kept block ids of units [id0, id0 + 64), one per lane
     for (int u = u0; u < u1; ++u) {
+        const int qq = wave;  // this wave's quarter (slice) of every unit
         int tok0, cnt;
         uint32_t hmask = (1u << G) - 1u;  // heads that take this unit
         if (u < nsel) {
@@ -284,7 +292,11 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         }
         tok0 = __builtin_amdgcn_readfirstlane(tok0);
         cnt = __builtin_amdgcn_readfirstlane(cnt);
-        const uint32_t soff = (uint32_t)tok0 * (uint32_t)a.skv_t * 2u;
+        const int wt0 = qq * TPW;  // first token of this slice inside its unit
+        if constexpr (!GT) {
+            if (wt0 >= cnt) continue;  // a slice of the tail past the context: nothing to attend
+        }
+        const uint32_t soff = (uint32_t)(tok0 + wt0) * (uint32_t)a.skv_t * 2u;
         // The tail unit's rows at or past the context end re-read its last token:
         // they take no weight, and they are neither read past the cache (the range
         // check covers only the per-lane offset) nor able to bring a non-finite

@@ -48,7 +48,7 @@ class DecodePlan:
         dws = seer.seer_sparse_decode_workspace_size(s.B, s.Hq, s.Hkv, s.d, s.k_max, s.bs, self.num_splits)
         self.decode_ws = torch.empty((max(dws, 16) + 3) // 4, dtype=torch.float32, device=dev)
         sws = seer.seer_decode_step_workspace_size(s.B, s.Hq, s.Hkv, s.d, s.k_max, s.bs, self.num_splits)
-        # zero-filled once: the step's counters return to zero after every launch
+        # zero-filled once: the step's merge counters return to zero after every launch
         self.step_ws = torch.zeros((max(sws, 16) + 3) // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((s.B, s.Hq, s.d), dtype=out_dtype, device=dev)
         self.lse = torch.empty((s.B, s.Hq), dtype=torch.float32, device=dev)
@@ -78,7 +78,8 @@ class DecodePlan:
 
         mode "calls" (the default, the fastest form measured): seer_gate_scores, seer_select_blocks,
         seer_sparse_decode; "gate_select": seer_gate_select then seer_sparse_decode;
-        "fused": one persistent launch (seer_decode_step), bit-for-bit the "calls" results."""
+        "fused": seer_decode_step (gate, then select + decode + merge in one launch), bit-for-bit the
+        "calls" results."""
         if mode == "fused":
             s = self.shape
             seer.seer_decode_step(q, k, v, seqlens, kpool, wq, wk, s.bs, s.budget, self.gate_scale,
@@ -117,10 +118,6 @@ class DecodePlan:
                                              self.out, self.lse, self.decode_ws, self.num_splits, stream=stream,
                                              bind=True))
         return calls
-
-    def step_status(self, stream=None) -> int:
-        """0 while every fused step on this plan's workspace ran to completion."""
-        return seer.seer_decode_step_status(self.step_ws, stream=stream)
 
 
 def full_pool_lists(seqlens_host: torch.Tensor, bs: int, device="cuda"):

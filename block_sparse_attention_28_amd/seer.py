@@ -65,7 +65,6 @@ SIGNATURES = {
     "seer_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_decode_step": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _F, _P, _I, _I, _I, _I,
                               _I, _I, _I, _F, _I, _P, _P, _P, _P, _SZ, _P, _I, _P, _P]),
-    "seer_decode_step_status": (_I, [_P, _P, _P]),
     "seer_block_sparse_prefill_kmax_row": (_I, [_I, _I, _I, _I]),
     "seer_block_sparse_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "seer_block_sparse_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _F, _I, _I, _P, _P, _I, _I, _F,
@@ -409,9 +408,3 @@ def seer_decode_step(q, k, v, seqlens, kpool, wq, wk, block_size: int, budget_to
         Hq, Hkv, d, block_size, int(budget_tokens), float(softmax_scale), int(num_splits), _ptr(scores),
         _ptr(block_idx) if k_max else None, _ptr(n_sel), _ptr(workspace), ws_bytes, _ptr(out), out_dtype, _ptr(lse),
         _stream(stream), bind=bind)
-
-
-def seer_decode_step_status(workspace, stream=None) -> int:
-    st = C.c_int(-1)
-    _call("seer_decode_step_status", _ptr(workspace), C.byref(st), _stream(stream))
-    return st.value

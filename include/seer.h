@@ -298,25 +298,20 @@ int seer_decode_block_mass(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                            float *mass, hipStream_t stream);
 
 /*
- * One whole decode step in a single launch: the gate scores, the token-budget
- * selection and the sparse decode with its merge -- the same results, bit for
- * bit, as seer_gate_scores + seer_select_blocks + seer_sparse_decode with the
- * same arguments, but run by one persistent grid: each decode split of a
- * (b, KV head) starts as soon as that pair's gate scores are complete, selects
- * the pair's blocks itself in LDS and decodes (no kernel boundaries in
- * between).
+ * One whole decode step: the gate scores, the token-budget selection and the
+ * sparse decode with its merge, in two kernel launches instead of four: the
+ * gate scores, then one kernel whose workgroups select their (b, KV head)'s
+ * blocks in LDS, decode their split and, the last split of each (b, KV head),
+ * merge the splits.  The results equal those of seer_gate_scores +
+ * seer_select_blocks + seer_sparse_decode with the same arguments bit for bit.
  *   arguments as in the three calls above; scores [B][Hkv][nb_max],
  *   block_idx [B][Hkv][budget_tokens / block_size] and n_sel [B][Hkv] are
  *   written as those calls write them.
- *   workspace >= seer_decode_step_workspace_size(...) bytes: control words and
- *              per-pair counters, then the split partials.  It must be
- *              zero-filled before its first use; every call leaves the
- *              counters at zero again.  Calls sharing a workspace must be
- *              ordered on one stream.
- * Every wait inside the launch is bounded: if one ever ran out (it cannot in a
- * correct launch), the launch still ends, its results are invalid, and
- * seer_decode_step_status reports 1 until the workspace is zero-filled again.
- * nb_max <= 16128.
+ *   workspace >= seer_decode_step_workspace_size(...) bytes: one counter per
+ *              (b, KV head), then the split partials.  It must be zero-filled
+ *              before its first use; every call leaves the counters at zero
+ *              again.  Calls sharing a workspace must be ordered on one stream.
+ * nb_max <= 16128; B * Hkv <= 65535.
  */
 size_t seer_decode_step_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
                                        int num_splits);
@@ -329,8 +324,6 @@ int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                      float *scores, int32_t *block_idx, int32_t *n_sel,
                      void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
                      hipStream_t stream);
-/* Copies the step workspace's status word (0 = valid) to *status and synchronises `stream`. */
-int seer_decode_step_status(const void *workspace, int *status, hipStream_t stream);
 
 /*
  * Block-sparse causal prefill (SeerAttention, abstract v1: the gate pools Q and

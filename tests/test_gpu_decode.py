@@ -159,30 +159,35 @@ FUSED_CASES = [TINY_DECODE, DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE,
                DecodeWorkload(name="fused_empty", B=2, Hq=4, Hkv=1, d=128, bs=64, budget=0, seed=32, L=256)]
 
 
+def assert_same_step(fused, sep, what):
+    """The two-launch step against the separate calls: every output bit for bit."""
+    for n, a, b in zip(("scores", "block_idx", "n_sel", "out", "lse"), fused, sep):
+        assert torch.equal(a, b), f"{what}: {n} differs between the fused and the separate path"
+
+
 @pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
 def test_fused_step_equals_separate_calls(w):
-    """seer_decode_step gives bit-for-bit the results of gate + select + decode launched separately,
-    twice in a row on one workspace (its counters must be back at zero after each launch)."""
+    """seer_decode_step (gate launch, then select + decode + merge in one launch) against gate +
+    select + decode launched separately, twice in a row on one workspace (its counters must be
+    back at zero after each launch)."""
     run = build_and_run(w, mode="fused")
     p = run.plan
-    assert p.step_status() == 0
     fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(run.q, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"],
            run.cache["wk"], mode="calls")
     torch.cuda.synchronize()
     sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
-    names = ("scores", "block_idx", "n_sel", "out", "lse")
-    for n, a, b in zip(names, fused, sep):
-        assert torch.equal(a, b), f"{n} differs between the fused and the separate path"
+    assert_same_step(fused, sep, w.name)
     q2 = inputs.decode_query(w, 1, "cuda")
     p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
            mode="fused")
     torch.cuda.synchronize()
-    o2 = p.out.clone()
+    fused2 = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
            mode="calls")
     torch.cuda.synchronize()
-    assert torch.equal(o2, p.out) and p.step_status() == 0
+    assert_same_step(fused2, [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], w.name + " #2")
+    assert torch.all(p.step_ws.view(torch.int32)[:w.B * w.Hkv] == 0), "step counters not back at zero"
 
 
 def test_step_replays_as_hip_graph():
@@ -212,23 +217,21 @@ def test_step_replays_as_hip_graph():
 
 
 @pytest.mark.parametrize("splits", [4, 8])
-def test_fused_step_over_several_rounds(splits):
-    """More (pair, split) items than resident workgroups: 128 x 8 pairs at 4 and 8 splits are 4096
-    and 8192 items, above the 2048 workgroups of 256 threads that 256 compute units can hold, so the
-    persistent grid takes each pair's splits in a later round.  Bit-exact against the separate
-    calls, twice in a row on one workspace."""
+def test_fused_step_many_workgroups(splits):
+    """128 x 8 pairs at 4 and 8 splits: 4096 and 8192 workgroups, more than the compute units hold
+    at once, so a pair's splits run in different dispatch rounds before the last one merges.
+    Against the separate calls, twice in a row on one workspace."""
     w = DecodeWorkload(name="fused_rounds", B=128, Hq=16, Hkv=8, d=64, bs=64, budget=512, seed=33,
                        L_range=(600, 4000))
     run = build_and_run(w, num_splits=splits, mode="fused")
     p = run.plan
-    assert p.num_splits == splits and p.step_status() == 0
+    assert p.num_splits == splits
     args = (run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"])
     fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(run.q, *args, mode="calls")
     torch.cuda.synchronize()
-    for n, a, b in zip(("scores", "block_idx", "n_sel", "out", "lse"), fused,
-                       (p.scores, p.block_idx, p.n_sel, p.out, p.lse)):
-        assert torch.equal(a, b), f"{n} differs between the fused and the separate path"
+    sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    assert_same_step(fused, sep, "first")
     p.step(run.q, *args, mode="fused")
     torch.cuda.synchronize()
-    assert torch.equal(p.out, fused[3]) and torch.equal(p.lse, fused[4]) and p.step_status() == 0
+    assert_same_step([t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], sep, "second")
