@@ -1,8 +1,11 @@
-"""Compile the gfx950 HIP library (libseer.so) in-tree with hipcc.
+"""Compile the gfx950 HIP libraries in-tree with hipcc.
 
 Every HIP source under csrc/ is compiled to an object for gfx950 only, then
-linked into block_sparse_attention_28_amd/libseer.so.  Packed fp32 VALU ops
-are disabled for all device code.
+linked into block_sparse_attention_28_amd/libseer.so; the benchmark's
+measurement probes (probes/) go into libseer_probe.so.  Packed fp32 VALU ops
+are disabled for all device code: the flag reaches hipcc's host pass too
+(hipcc cannot forward an option that takes an argument to the device pass
+alone), which ignores it with a warning.
 """
 from __future__ import annotations
 
@@ -18,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libseer.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libseer_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -46,17 +51,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Builds libseer.so (the method) and libseer_probe.so (the benchmark's measurement probes)."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(PROBES, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs) + len(probes)))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     return LIB
 
 

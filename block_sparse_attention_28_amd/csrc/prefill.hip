@@ -384,20 +384,31 @@ __global__ __launch_bounds__(256) void prefill_select_rows_kernel(const float *S
 
 // ----------------------------------------------------------- attention ----
 // Workgroup of 4 waves per 64-row query block.  Wave w owns query rows
-// 32 * (w & 1) + 0..31 (two 16-row MFMA tiles) and keys 32 * (w >> 1) + 0..31 of
-// every kept key block, so each K / V element staged in LDS is read by two
-// waves instead of four; the two key halves of a row are merged once at the end
-// (their running maxima and sums combine as in split-KV decoding).
+// 32 (w & 1) + 0..31 and keys 32 (w >> 1) + 0..31 of every kept key block, so
+// each K / V element staged in LDS is read by two waves instead of four; the
+// two key halves of a row are merged once at the end (their running maxima and
+// sums combine as in split-KV decoding).
 //
-// LDS layouts (one 64-key block of 256-byte rows; bank behaviour measured on
-// gfx950).  Both are filled by buffer_load ... lds, which writes lane l's 16
-// bytes at the wave's LDS base + 16 l, so a swizzle is a choice of which
-// global chunk each lane loads.
-//  K : 16-byte chunk c of key r at chunk c ^ (r & 15): the 16 keys x 16 bytes
-//      of an MFMA A operand read hit distinct banks.
-//  V : 32-byte chunk c (columns 16c..16c+15) of key r at chunk c ^ (r & 7):
-//      the transposing reads (ds_read_b64_tr_b16) that build the V^T operand
-//      from 16 keys x 32 bytes hit distinct banks.
+// Both products run on v_mfma_f32_32x32x16_bf16, which this part sustains at
+// about twice the rate of the 16x16x32 shape:
+//   S^T = K Q^T   A = 32 keys x 16 dims (one 16-byte K chunk per lane), B = Q^T
+//                 held in registers.  Lane l ends with query row l % 32 and the
+//                 wave's keys 8 a + 4 hl + b (a, b = 0..3, hl = l / 32).
+//   O^T = V^T P^T B = P^T: k-step s takes the lane's own keys with a = 2 s and
+//                 2 s + 1, so the weights never move between lanes; A = V^T, two
+//                 ds_read_b64_tr_b16 per lane from the 4-key groups 16 s + 4 hl
+//                 (k slots 8 hl + 0..3) and 16 s + 8 + 4 hl (slots 8 hl + 4..7),
+//                 exactly those keys.
+//   A query row's statistics live in two lanes (l and l ^ 32): one swap each.
+//
+// LDS layouts (one 64-key block of 256-byte rows).  buffer_load ... lds writes
+// lane l's 16 bytes at the wave's LDS base + 16 l, so a swizzle is a choice of
+// which global chunk each lane loads.
+//  K : 16-byte chunk c of key r at slot c ^ (r & 15): an A operand read (32
+//      keys, one chunk) hits distinct banks in each 16-lane phase.
+//  V : 32-byte chunk c of key r at chunk c ^ 2 (r & 3): a transposing read
+//      covers 4 consecutive keys x 2 adjacent chunks per 32 lanes, which land in
+//      8 distinct chunks.
 
 // GT (the ground-truth form): every causal block j <= i is attended (the lists
 // are not read), and after the output a second sweep over K recomputes the
@@ -411,17 +422,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                                                                    float scale_log2, uint16_t *out, float *lse,
                                                                    float *mass) {
     static_assert(D == 128, "the LDS layouts assume 256-byte key rows");
-    constexpr int KS = D / 32;           // k-steps of S^T = K Q^T
-    constexpr int DT = D / 16;           // 16-wide d tiles of O^T
-    constexpr int CPR = D / 8;           // 16-byte chunks per key row
+    typedef float f32x16_t __attribute__((ext_vector_type(16)));
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    constexpr int KS = D / 16;           // k-steps of S^T = K Q^T
+    constexpr int DT = D / 32;           // 32-wide d tiles of O^T
     constexpr int KBYTES = kPBS * D * 2;
     constexpr int DMA_PER_WAVE = KBYTES / 1024 / 4;  // 1 KiB buffer_load ... lds per wave and tensor
     // Two K and two V buffers (separate objects, so that the compiler sees a load
     // into one buffer does not alias reads of another); the key-half exchange
-    // (2 tiles x DT x 256 floats per row half) reuses the K buffers after the sweep.
+    // (DT x 16 floats per lane of a row half) reuses the K buffers after the sweep.
     __shared__ __align__(16) char kbuf0[KBYTES], kbuf1[KBYTES], vbuf0[KBYTES], vbuf1[KBYTES];
-    __shared__ float xml[2][2][2][64];   // [rh][tile][m | l][lane] of the key-half-1 waves
-    static_assert(2 * DT * 256 * 4 <= KBYTES, "one row half's exchange fits a K buffer");
+    __shared__ float xml[2][2][64];   // [rh][m | l][lane] of the key-half-1 waves
+    static_assert(DT * 16 * 64 * 4 <= KBYTES, "one row half's exchange fits a K buffer");
 
     // Workgroups reach the 8 XCDs round-robin (id % 8); give each XCD one
     // contiguous range of the (b, h)-major list so that a head's K / V blocks
@@ -437,28 +449,25 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rh = wave & 1, kh = wave >> 1;
-    const int g = lane >> 4, n = lane & 15;
+    const int hl = lane >> 5, n = lane & 31;
     const int64_t head = ((int64_t)b * H + h) * L * D;
     const uint16_t *qh = q + head, *kh_ptr = k + head, *vh = v + head;
-    int qtok[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) qtok[r] = i * kPBS + 32 * rh + 16 * r + n;  // this lane's query rows
+    const int qtok = i * kPBS + 32 * rh + n;  // this lane's query row
 
-    bf16x8_t qop[2][KS];
+    // B operand of S^T: lane (hl, n) holds dims 16 ks + 8 hl .. + 7 of query row qtok.
+    bf16x8_t qop[KS];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint4 w = qtok < L ? *reinterpret_cast<const uint4 *>(qh + (int64_t)qtok * D + 16 * ks + 8 * hl)
+                                 : make_uint4(0, 0, 0, 0);
+        qop[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    f32x16_t oacc[DT];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 w = qtok[r] < L ? *reinterpret_cast<const uint4 *>(qh + (int64_t)qtok[r] * D + 8 * g + 32 * ks)
-                                  : make_uint4(0, 0, 0, 0);
-            qop[r][ks] = __builtin_bit_cast(bf16x8_t, w);
-        }
-    f32x4_t oacc[2][DT];
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[r][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+        for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, m_ref = 0.f;
 
     const int64_t row = ((int64_t)b * H + h) * nb + i;
     int cnt = GT ? i + 1 : kv_count[row];
@@ -484,7 +493,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         const int r = 16 * wave + 4 * qd + (lane >> 4), s = lane & 15;
         drow[qd] = r;
         kdv[qd] = (uint32_t)(r * D * 2 + ((s ^ (r & 15)) << 4));
-        vdv[qd] = (uint32_t)(r * D * 2 + (((((s >> 1) ^ (r & 7)) << 1) | (s & 1)) << 4));
+        vdv[qd] = (uint32_t)(r * D * 2 + (((((s >> 1) ^ (2 * (r & 3))) << 1) | (s & 1)) << 4));
     }
     auto block_start = [&](int it) {
         int j = block_of(it);
@@ -509,22 +518,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         }
     };
     auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's loads are in LDS
-    // S^T[key][qrow] of this wave's 32 keys and 32 rows: s[r][t] holds keys
-    // 32kh + 16t + 4g + e of query row qtok[r]; each K operand serves both tiles.
-    auto scores = [&](f32x4_t (&s)[2][2], const char *kb) {
+    // S^T of this wave's 32 keys and 32 query rows: s[4 a + b] holds key
+    // 32 kh + 8 a + 4 hl + b of query row qtok.
+    auto scores = [&](f32x16_t &s, const char *kb) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+        const char *krow_lds = kb + (32 * kh + n) * (D * 2);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) s[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const char *krow_lds = kb + (32 * kh + 16 * t + n) * (D * 2);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((g + 4 * ks) ^ n) << 4));
-#pragma unroll
-                for (int r = 0; r < 2; ++r) s[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[r][ks], s[r][t], 0, 0, 0);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((2 * ks + hl) ^ (n & 15)) << 4));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s, 0, 0, 0);
         }
     };
     // Causal / length masks: only the diagonal block and a partial last block need them.
@@ -532,95 +535,78 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         const int k0 = block_start(it);
         return k0 == i * kPBS || k0 + kPBS > L;
     };
-    auto mask = [&](f32x4_t (&s)[2][2], int it) {
+    auto mask = [&](f32x16_t &s, int it) {
         const int k0 = block_start(it);
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ktok = k0 + 32 * kh + 16 * t + 4 * g + e;
-                    if (ktok > qtok[r] || ktok >= L) s[r][t][e] = -INFINITY;
-                }
-    };
-    // Running maximum with lazy rescaling: the reference m_run[r] moves only
-    // when the block's maximum exceeds it by more than kLazyRescale (log2
-    // units), so the weights stay below 2^kLazyRescale and O is rarely
-    // rescaled.  Any reference gives the same softmax once O is divided by l.
-    // m_ref[r] is m_run[r], or 0 while that is -inf.  Each lane first tests its
-    // own scores: rounding is monotone, so some lane's max * scale exceeds the
-    // bound exactly when the row's max * scale does, and the cross-lane
-    // reductions run only in the (rare) blocks where a reference moves.
-    float m_ref[2] = {0.f, 0.f};
-    auto prep = [&](const f32x4_t (&s)[2][2], bool live) {
-        float lmax[2];
-        bool need = false;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            lmax[r] = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) lmax[r] = fmax_fast(lmax[r], s[r][t][e]);
-            need |= live && lmax[r] * scale_log2 > m_run[r] + kLazyRescale;  // always when m_run is still -inf
+        for (int e = 0; e < 16; ++e) {
+            const int ktok = k0 + 32 * kh + 8 * (e >> 2) + 4 * hl + (e & 3);
+            if (ktok > qtok || ktok >= L) s[e] = -INFINITY;
         }
+    };
+    // Running maximum with lazy rescaling: the reference m_run moves only when
+    // the block's maximum exceeds it by more than kLazyRescale (log2 units), so
+    // the weights stay below 2^kLazyRescale and O is rarely rescaled.  Any
+    // reference gives the same softmax once O is divided by l.  m_ref is m_run,
+    // or 0 while that is -inf.  Each lane first tests its own scores: rounding
+    // is monotone, so some lane's max * scale exceeds the bound exactly when the
+    // row's max * scale does, and the partner exchange and the rescale run only
+    // in the (rare) blocks where a reference moves.
+    auto prep = [&](const f32x16_t &s, bool live) {
+        float lmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) lmax = fmax_fast(lmax, s[e]);
+        const bool need = live && lmax * scale_log2 > m_run + kLazyRescale;  // always when m_run is still -inf
         if (!__ballot(need)) return;
+        const float mloc = max_xor32(lmax) * scale_log2;  // the two lanes of this query row
+        const bool bump = live && mloc > m_run + kLazyRescale;
+        const float m_new = bump ? mloc : m_run;
+        const float ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = bump ? fast_exp2(m_run - ref) : 1.0f;
+        m_run = m_new;
+        m_ref = ref;
+        if (__ballot(bump)) {  // some row's reference moved
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float mloc = max_xor32(max_xor16(lmax[r])) * scale_log2;  // the 4 lanes of this query row
-            const bool bump = live && mloc > m_run[r] + kLazyRescale;
-            const float m_new = bump ? mloc : m_run[r];
-            const float ref = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = bump ? fast_exp2(m_run[r] - ref) : 1.0f;
-            m_run[r] = m_new;
-            m_ref[r] = ref;
-            if (__ballot(bump)) {  // some row's reference moved
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[r][dt] *= alpha;
-                l_run[r] *= alpha;
-            }
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            l_run *= alpha;
         }
     };
-    // Weights of one block (relative to m_ref) into the P^T operands:
-    // k-slots 8g..8g+3 <- keys 4g + e, 8g+4..8g+7 <- keys 16 + 4g + e (of the half).
-    auto weights = [&](f32x4_t (&s)[2][2], bf16x8_t (&pb)[2]) {
+    // Weights of one block (relative to m_ref) into the P^T operands of the two
+    // k-steps: pb[s] = weights s[8 s .. 8 s + 7].
+    auto weights = [&](f32x16_t &s, bf16x8_t (&pb)[2]) {
+        float lsum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            float lsum = 0.f;
+        for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(fmaf(s[e], scale_log2, -m_ref));
+            s[e] = p;
+            lsum += p;
+        }
+        l_run += lsum;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = fast_exp2(fmaf(s[r][t][e], scale_log2, -m_ref[r]));
-                    s[r][t][e] = p;
-                    lsum += p;
-                }
-            l_run[r] += lsum;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pb[r][e] = (__bf16)s[r][0][e];
-                pb[r][4 + e] = (__bf16)s[r][1][e];
-            }
+        for (int e = 0; e < 8; ++e) {
+            pb[0][e] = (__bf16)s[e];
+            pb[1][e] = (__bf16)s[8 + e];
         }
     };
-    // V^T operand of d tile dt: two transposing reads giving keys
-    // 32kh + 16h + 4g + e (h = 0, 1; e = 0..3) of column 16dt + n, the k-slot
-    // order of P^T.  Lane (g, s) points at row 32kh + 4g + s / 4 (+ 16 for h = 1),
-    // columns 16dt + 4 (s % 4) + 0..3; rows 32kh + 4g + s / 4 and + 16 share r & 7.
-    const int vrow_rd = 32 * kh + 4 * g + (n >> 2), vx = vrow_rd & 7;
+    // V^T operand of d tile dt and k-step s: lane (hl, dg, j) (j = lane % 16,
+    // dg = lane / 16 % 2) points at key 32 kh + 16 s + 4 hl + j / 4 (and + 8),
+    // columns 32 dt + 16 dg + 4 (j % 4) + 0..3; after the transpose it holds
+    // column 32 dt + 16 dg + j of 4 keys.  The key's swizzle 2 (r & 3) is
+    // 2 (j / 4) for every such key.
+    const int tj = lane & 15, tdg = (lane >> 4) & 1;
+    const int vrow_rd = 32 * kh + 4 * hl + (tj >> 2);
     auto pv = [&](const bf16x8_t (&pb)[2], const char *vb) {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        const char *vr = vb + vrow_rd * (D * 2) + (n & 3) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const char *p = vr + ((dt ^ vx) << 5);
-            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
-            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s *)(p + 16 * D * 2));
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const char *pcol = vb + vrow_rd * (D * 2) + ((dt ^ (tj >> 2)) << 6) + (tdg << 5) + ((tj & 3) << 3);
 #pragma unroll
-            for (int r = 0; r < 2; ++r) oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[r], oacc[r][dt], 0, 0, 0);
+            for (int st = 0; st < 2; ++st) {
+                const char *p = pcol + 16 * st * (D * 2);
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s *)(p + 8 * D * 2));
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], oacc[dt], 0, 0, 0);
+            }
         }
     };
 
@@ -631,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // of block it + 1 into the buffers the last iteration finished with; they
     // land while it computes.  One barrier per iteration.  Buffer parity follows
     // it, so the loop is unrolled by two.
-    f32x4_t sA[2][2], sB[2][2];
+    f32x16_t sA, sB;
     if (cnt > 0) {
         dma(0, kbuf0, krs, kdv);
         dma(0, vbuf0, vrs, vdv);
@@ -645,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     }
     // s_cur holds block it's masked scores with its reference applied to O and
     // l; s_next receives block it + 1.  P = it & 1 (compile-time).
-    auto step = [&](auto par, int it, f32x4_t (&s_cur)[2][2], f32x4_t (&s_next)[2][2]) {
+    auto step = [&](auto par, int it, f32x16_t &s_cur, f32x16_t &s_next) {
         constexpr int P = decltype(par)::value;
         char *const k_this = P ? kbuf1 : kbuf0, *const k_next = P ? kbuf0 : kbuf1;
         char *const v_this = P ? vbuf1 : vbuf0, *const v_next = P ? vbuf0 : vbuf1;
@@ -671,59 +657,53 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
 
     // Merge the two key halves of each row: the kh = 1 waves hand (m, l, O) to
     // their kh = 0 partners through LDS.
-    float l_row[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) l_row[r] = sum_xor32(sum_xor16(l_run[r]));
-    float *xo = reinterpret_cast<float *>(rh ? kbuf1 : kbuf0);  // per row half: 2 tiles x DT x 256 floats
+    const float l_row = sum_xor32(l_run);
+    float *xo = reinterpret_cast<float *>(rh ? kbuf1 : kbuf0);  // per row half: [dt][lane][16] floats
     __syncthreads();  // the staging area is free
     if (kh == 1) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4_t *>(xo + (r * DT + dt) * 256 + lane * 4) = oacc[r][dt];
-            xml[rh][r][0][lane] = m_run[r];
-            xml[rh][r][1][lane] = l_row[r];
-        }
+            for (int e4 = 0; e4 < 4; ++e4)
+                *reinterpret_cast<f32x4_t *>(xo + (dt * 64 + lane) * 16 + 4 * e4) =
+                    f32x4_t{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
+        xml[rh][0][lane] = m_run;
+        xml[rh][1][lane] = l_row;
     }
     __syncthreads();
-    float lse2[2];  // final log2-domain row log-sum-exp (kh = 0 waves)
+    float lse2 = 0.f;  // final log2-domain row log-sum-exp (kh = 0 waves)
     if (kh == 0) {
+        const float m1 = xml[rh][0][lane], l1 = xml[rh][1][lane];
+        const float m = fmax_fast(m_run, m1);
+        const float mr = m == -INFINITY ? 0.f : m;
+        const float a0 = fast_exp2(m_run - mr), a1 = fast_exp2(m1 - mr);
+        const float l_tot = l_row * a0 + l1 * a1;
+        lse2 = l_tot > 0.f ? m + log2f(l_tot) : INFINITY;
+        if (qtok < L) {
+            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+            uint16_t *orow = out + head + (int64_t)qtok * D;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float m1 = xml[rh][r][0][lane], l1 = xml[rh][r][1][lane];
-            const float m = fmax_fast(m_run[r], m1);
-            const float m_ref = m == -INFINITY ? 0.f : m;
-            const float a0 = fast_exp2(m_run[r] - m_ref), a1 = fast_exp2(m1 - m_ref);
-            const float l_tot = l_row[r] * a0 + l1 * a1;
-            lse2[r] = l_tot > 0.f ? m + log2f(l_tot) : INFINITY;
-            if (qtok[r] < L) {
-                const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-                uint16_t *orow = out + head + (int64_t)qtok[r] * D;
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + (r * DT + dt) * 256 + lane * 4);
-                    const f32x4_t o = (oacc[r][dt] * a0 + o1 * a1) * inv;
+                for (int e4 = 0; e4 < 4; ++e4) {  // d = 32 dt + 8 e4 + 4 hl + 0..3
+                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + (dt * 64 + lane) * 16 + 4 * e4);
+                    const f32x4_t o0 = f32x4_t{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2],
+                                               oacc[dt][4 * e4 + 3]};
+                    const f32x4_t o = (o0 * a0 + o1 * a1) * inv;
                     const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
                     const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-                    *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * g) = make_uint2(w0, w1);
+                    *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * e4 + 4 * hl) = make_uint2(w0, w1);
                 }
-                if (g == 0 && lse) lse[((int64_t)b * H + h) * L + qtok[r]] = l_tot > 0.f ? lse2[r] * kLn2 : -INFINITY;
-            }
+            if (hl == 0 && lse) lse[((int64_t)b * H + h) * L + qtok] = l_tot > 0.f ? lse2 * kLn2 : -INFINITY;
         }
     }
     if constexpr (GT) {
         // Second sweep: each block's share of every row's softmax, averaged over the block's rows.
         __shared__ float row_lse2[64];
         __shared__ float red[4];
-        if (kh == 0) {
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-                if (g == 0) row_lse2[32 * rh + 16 * r + n] = lse2[r];
-        }
+        if (kh == 0 && hl == 0) row_lse2[32 * rh + n] = lse2;
         __syncthreads();
-#pragma unroll
-        for (int r = 0; r < 2; ++r) lse2[r] = row_lse2[32 * rh + 16 * r + n];
+        lse2 = row_lse2[32 * rh + n];
         const int rows_i = L - i * kPBS < kPBS ? L - i * kPBS : kPBS;
         float *mrow = mass + row * nb;
         for (int jj = i + 1 + tid; jj < nb; jj += 256) mrow[jj] = 0.f;
@@ -733,19 +713,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
             dma(jb, kbuf0, krs, kdv);
             loads_done();
             __syncthreads();
-            f32x4_t s[2][2];
+            f32x16_t s;
             scores(s, kbuf0);
             float psum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int ktok = k0 + 32 * kh + 16 * t + 4 * g + e;
-                        const bool live = ktok <= qtok[r] && ktok < L && qtok[r] < L;
-                        psum += live ? fast_exp2(s[r][t][e] * scale_log2 - lse2[r]) : 0.f;
-                    }
+            for (int e = 0; e < 16; ++e) {
+                const int ktok = k0 + 32 * kh + 8 * (e >> 2) + 4 * hl + (e & 3);
+                const bool live = ktok <= qtok && ktok < L && qtok < L;
+                psum += live ? fast_exp2(s[e] * scale_log2 - lse2) : 0.f;
+            }
             psum = wave_sum(psum);
             if (lane == 0) red[wave] = psum;
             __syncthreads();
