@@ -30,8 +30,9 @@ sys.path.insert(0, ROOT)
 
 import torch  # noqa: E402
 
-from block_sparse_attention_28_amd import inputs, pipeline, seer  # noqa: E402
-from block_sparse_attention_28_amd.workloads import DECODE_WORKLOADS, DECODE_L64K_S90  # noqa: E402
+from block_sparse_attention_28_amd import inputs, pipeline, probe, seer  # noqa: E402
+from block_sparse_attention_28_amd.workloads import (DECODE_L32K, DECODE_L64K_S90, DECODE_WORKLOADS,  # noqa: E402
+                                                     RAGGED_DECODE, TINY_DECODE)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "sparse-decode effective KV GB/s (% of HBM peak) + us/step at 90% sparsity"
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--mode-steps", type=int, default=16, help="steps per form in the context timing (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=16, help="HIP-graph replays timed (0 = skip)")
     ap.add_argument("--dense", type=int, default=1, help="also time the decode with every block kept (context)")
+    ap.add_argument("--other", type=int, default=1, help="time the other decode workloads (context)")
+    ap.add_argument("--ceilings", type=int, default=1, help="measure the MFMA rate and the gather-read ceiling")
     return ap.parse_args()
 
 
@@ -279,6 +282,81 @@ def per_head_context(w, lay, step, plan, dev):
             "note": "every query head keeps its own blocks; the decode reads each group's union once"}
 
 
+def time_launches(fn, n, warm=3):
+    """Average microseconds of fn(i) over n calls on the current stream (HIP events)."""
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def decode_workload_context(w, dev, layers=3, steps=16):
+    """Another decode workload in the timed form (three calls) on rotated layers: the step and its
+    seer_sparse_decode launch (split + merge), with that launch's algorithmic bytes."""
+    lay = [Layer(w, l, 0, dev) for l in range(layers)]
+    base_L = lay[0].cache["seqlens"].cpu().to(torch.int64)
+    shape = pipeline.DecodeShape(w.B, w.Hq, w.Hkv, w.d, w.bs, w.budget, lay[0].nb_max, w.gate_dim)
+    plan = pipeline.DecodePlan(shape, dev)
+    calls = []
+    for l, ly in enumerate(lay):
+        ub, uj = pipeline.full_pool_lists(base_L, w.bs, dev)
+        plan.pool(ly.cache["k"], ly.kpool, ub, uj)
+        calls.append(plan.bind_step(inputs.decode_query(w, l, dev), ly.cache["k"], ly.cache["v"], ly.cache["seqlens"],
+                                    ly.kpool, ly.cache["wq"], ly.cache["wk"], mode="calls"))
+
+    def step(i):
+        for c in calls[i % layers]:
+            c()
+    us_step = time_launches(step, steps)
+    us_dec = time_launches(lambda i: calls[i % layers][-1](), steps)
+    _, alg = decode_bytes(w, base_L.tolist())
+    out = {"workload": w.name, "us_step": round(us_step, 2), "us_decode_launch": round(us_dec, 2),
+           "bytes_per_launch": int(alg), "num_splits": plan.num_splits}
+    if alg > 10_000_000:  # the tiny workload is latency-bound: microseconds only
+        gbps = alg / (us_dec * 1e-6) / 1e9
+        out.update({"achieved_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    del lay, plan, calls
+    torch.cuda.empty_cache()
+    return out
+
+
+def measured_ceilings(w, layers, plan, steps, dev):
+    """Context for the two rooflines: the bf16 MFMA rate this part sustains (both MFMA shapes the
+    kernels use, register operands only) and the read rate of the headline decode's own access
+    pattern (kept K/V blocks of each layer's first step streamed into LDS, no arithmetic)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {}
+    for shape, flops_per_wave_iter in ((16, 8 * 16384), (32, 4 * 32768)):
+        wg, iters = cus * 8, 2000
+        sink = torch.empty(wg * 256, device=dev)
+        us = time_launches(lambda i: probe.mfma_bf16(shape, sink, wg, iters), 3, warm=1)
+        res[f"mfma_bf16_{shape}x{shape}_tflops"] = round(wg * 4 * iters * flops_per_wave_iter / (us * 1e-6) / 1e12, 1)
+    R = len(layers)
+    idx = []
+    for l in range(R):
+        st = steps[l]
+        c = layers[st["layer"]].cache
+        plan.gate_select(st["q"], c["wq"], c["wk"], layers[st["layer"]].kpool, st["seqlens"])
+        idx.append(plan.block_idx.clone())
+    sink = torch.empty(w.B * w.Hkv * plan.num_splits, dtype=torch.int32, device=dev)
+    kept = min(w.k_max, min(st_L // w.bs for st_L in steps[0]["L"]))
+
+    def gather(i):
+        lay = layers[steps[i % R]["layer"]]
+        probe.gather_kv(lay.cache["k"], lay.cache["v"], idx[i % R], kept, w.bs, plan.num_splits, sink)
+    us = time_launches(gather, 32)
+    kv = w.B * w.Hkv * kept * w.bs * w.d * 2 * 2
+    res["gather_read"] = {"us": round(us, 2), "GBps": round(kv / (us * 1e-6) / 1e9, 1),
+                          "note": "the headline's kept K/V blocks streamed into LDS as the decode loads them"}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -374,7 +452,7 @@ def main():
     if mode == "fused":
         # one launch does the whole step: its algorithmic bytes include the gate's reads
         dom_bytes = mean_alg + gate_bytes(w, steps[W]["L"])
-        dom_name = "decode_step_kernel (seer_decode_step: gate, select, split decode, merge)"
+        dom_name = "seer_decode_step (gate kernel, then select + split decode + merge kernel)"
     else:
         dom_bytes = mean_alg
         dom_name = "seer_sparse_decode (split kernel + LSE merge kernel)"
@@ -403,6 +481,7 @@ def main():
     gt = ground_truth_context(w, layers[0], steps[0], plan, dev) if args.dense else None
     b16 = bf16_table_context(w, layers[0], steps[0], plan, dev, base_L) if args.dense else None
     ph = per_head_context(w, layers[0], steps[0], plan, dev) if args.dense else None
+    ceil = measured_ceilings(w, layers, plan, steps, dev) if args.ceilings else None
 
     line = {
         "metric": METRIC,
@@ -436,13 +515,18 @@ def main():
         "ground_truth": gt,
         "bf16_pooled_keys": b16,
         "per_head_selection": ph,
+        "ceilings": ceil,
     }
+    if ceil:
+        line["roofline"]["frac_of_gather_read"] = round(achieved / ceil["gather_read"]["GBps"], 4)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, layers[0], base_L, plan, args)
+    del layers, steps, plan
+    torch.cuda.empty_cache()
+    if args.other:
+        line["other_workloads"] = [decode_workload_context(ow, dev) for ow in (DECODE_L32K, RAGGED_DECODE, TINY_DECODE)]
     if args.prefill_steps > 0:
-        del layers
-        torch.cuda.empty_cache()
-        line["secondary_path"] = bench_prefill(args.prefill_steps, dev)
+        line["secondary_path"] = bench_prefill(args.prefill_steps, dev, ceil)
     print(json.dumps(line), flush=True)
 
 
@@ -457,7 +541,7 @@ def prefill_flops(counts, bs, d):
     return (kept - diag) * 4 * bs * bs * d + diag * 4 * (bs * (bs + 1) // 2) * d
 
 
-def bench_prefill(steps, dev):
+def bench_prefill(steps, dev, ceil=None):
     """Gate + MFMA attention of the 32k-token block-sparse causal prefill (keep 1/10)."""
     from block_sparse_attention_28_amd.workloads import PREFILL_L32K as pw
     x = inputs.prefill_inputs(pw, dev)
@@ -520,6 +604,8 @@ def bench_prefill(steps, dev):
             "roofline": {"kernel": "prefill_attention_kernel", "bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "frac_of_measured_32x32x16": (round(tflops / ceil["mfma_bf16_32x32_tflops"], 4)
+                                                       if ceil else None),
                          "traffic": measured_traffic(pw.name, "prefill_attention_traffic.json")}}
 
 

@@ -592,12 +592,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // columns 32 dt + 16 dg + 4 (j % 4) + 0..3; after the transpose it holds
     // column 32 dt + 16 dg + j of 4 keys.  The key's swizzle 2 (r & 3) is
     // 2 (j / 4) for every such key.
+    // The byte offset within the tile takes only the bits of rows 0..7 and
+    // 32..39 (0x2000, 0x0700) and of the chunk and column terms (0x00F8).  Masking
+    // it with exactly those bits changes nothing, but lets the compiler see that
+    // the reads stay inside this V buffer: otherwise it cannot rule out the
+    // in-flight loads into the other buffers and waits for them (vmcnt(0)) in
+    // the middle of every iteration.
     const int tj = lane & 15, tdg = (lane >> 4) & 1;
     const int vrow_rd = 32 * kh + 4 * hl + (tj >> 2);
+    constexpr int kVReadBits = 0x2000 | 0x0700 | 0x00F8;
     auto pv = [&](const bf16x8_t (&pb)[2], const char *vb) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const char *pcol = vb + vrow_rd * (D * 2) + ((dt ^ (tj >> 2)) << 6) + (tdg << 5) + ((tj & 3) << 3);
+            const char *pcol =
+                vb + ((vrow_rd * (D * 2) + ((dt ^ (tj >> 2)) << 6) + (tdg << 5) + ((tj & 3) << 3)) & kVReadBits);
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 const char *p = pcol + 16 * st * (D * 2);

@@ -9,6 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "seer.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "seer_probe.h")
 
 
 @pytest.fixture(scope="module")
@@ -19,8 +20,8 @@ def lib():
     return seer.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(seer_[a-z0-9_]+)\s*\(", text)))
 
@@ -35,6 +36,20 @@ def test_header_declares_the_five_calls():
 def test_every_declared_symbol_is_exported(lib):
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's measurement probes (a separate library, not the method's ABI)."""
+    from block_sparse_attention_28_amd import build, probe
+    if not os.path.exists(probe._PATH):
+        build.build()
+    plib = probe.load()
+    names = declared_functions(PROBE_HEADER)
+    assert names == sorted(probe.SIGNATURES)
+    assert all(hasattr(plib, n) for n in names)
+    # argument checks run before any launch
+    assert plib.seer_probe_mfma_bf16(24, FAKE, 8, 1, NULL) == -1
+    assert plib.seer_probe_gather_kv(FAKE, FAKE, 0, 0, 1024, FAKE, 4, 5, 2, 8, 128, 4, FAKE, NULL) == -1
 
 
 def test_binding_signatures_cover_the_header(lib):
