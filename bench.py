@@ -332,7 +332,7 @@ def measured_ceilings(w, layers, plan, steps, dev):
     pattern (kept K/V blocks of each layer's first step streamed into LDS, no arithmetic)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     res = {}
-    for shape, flops_per_wave_iter in ((16, 8 * 16384), (32, 4 * 32768)):
+    for shape, flops_per_wave_iter in ((16, 16 * 16384), (32, 8 * 32768)):
         wg, iters = cus * 8, 2000
         sink = torch.empty(wg * 256, device=dev)
         us = time_launches(lambda i: probe.mfma_bf16(shape, sink, wg, iters), 3, warm=1)

@@ -519,16 +519,25 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     };
     auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's loads are in LDS
     // S^T of this wave's 32 keys and 32 query rows: s[4 a + b] holds key
-    // 32 kh + 8 a + 4 hl + b of query row qtok.
+    // 32 kh + 8 a + 4 hl + b of query row qtok.  The even and odd k-steps
+    // accumulate separately (two independent MFMA chains instead of one chain
+    // of 8) and are added at the end.
     auto scores = [&](f32x16_t &s, const char *kb) {
+        f32x16_t s1;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+        for (int e = 0; e < 16; ++e) {
+            s[e] = 0.f;
+            s1[e] = 0.f;
+        }
         const char *krow_lds = kb + (32 * kh + n) * (D * 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((2 * ks + hl) ^ (n & 15)) << 4));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s, 0, 0, 0);
+        for (int ks = 0; ks < KS; ks += 2) {
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((2 * ks + hl) ^ (n & 15)) << 4));
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((2 * ks + 2 + hl) ^ (n & 15)) << 4));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[ks], s, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[ks + 1], s1, 0, 0, 0);
         }
+        s += s1;
     };
     // Causal / length masks: only the diagonal block and a partial last block need them.
     auto is_edge = [&](int it) {
@@ -666,14 +675,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // Merge the two key halves of each row: the kh = 1 waves hand (m, l, O) to
     // their kh = 0 partners through LDS.
     const float l_row = sum_xor32(l_run);
-    float *xo = reinterpret_cast<float *>(rh ? kbuf1 : kbuf0);  // per row half: [dt][lane][16] floats
+    float *xo = reinterpret_cast<float *>(rh ? kbuf1 : kbuf0);  // per row half: [dt][e4][lane][4] floats
     __syncthreads();  // the staging area is free
     if (kh == 1) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
-                *reinterpret_cast<f32x4_t *>(xo + (dt * 64 + lane) * 16 + 4 * e4) =
+                *reinterpret_cast<f32x4_t *>(xo + ((dt * 4 + e4) * 64 + lane) * 4) =
                     f32x4_t{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
         xml[rh][0][lane] = m_run;
         xml[rh][1][lane] = l_row;
@@ -694,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {  // d = 32 dt + 8 e4 + 4 hl + 0..3
-                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + (dt * 64 + lane) * 16 + 4 * e4);
+                    const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(xo + ((dt * 4 + e4) * 64 + lane) * 4);
                     const f32x4_t o0 = f32x4_t{oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2],
                                                oacc[dt][4 * e4 + 3]};
                     const f32x4_t o = (o0 * a0 + o1 * a1) * inv;

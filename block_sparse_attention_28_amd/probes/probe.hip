@@ -19,7 +19,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kChains = 8;  // independent accumulators per wave
+constexpr int kChains = 16;  // independent accumulators per wave
 
 __global__ __launch_bounds__(256) void mfma_16x16x32_kernel(float *sink, int iters) {
     const int t = threadIdx.x;

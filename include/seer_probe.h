@@ -16,9 +16,9 @@
 extern "C" {
 #endif
 
-/* Matrix-core rate: `workgroups` x 256 threads, each wave issuing `iters` x 8
+/* Matrix-core rate: `workgroups` x 256 threads, each wave issuing `iters` x 16
  * independent v_mfma_f32_16x16x32_bf16 (shape 16: 16384 flops each) or
- * `iters` x 4 v_mfma_f32_32x32x16_bf16 (shape 32: 32768 flops each) on register
+ * `iters` x 8 v_mfma_f32_32x32x16_bf16 (shape 32: 32768 flops each) on register
  * operands.  sink: float [workgroups * 256], written once per thread. */
 int seer_probe_mfma_bf16(int shape, float *sink, int workgroups, int iters, hipStream_t stream);
 
