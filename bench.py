@@ -67,17 +67,28 @@ class Layer:
         self.kpool = torch.zeros((w.B, w.Hkv, self.nb_max, w.d), dtype=torch.float32, device=device)
 
 
+def code_sha256(files):
+    """sha256 over the given C/HIP sources with comments and white space removed, so that
+    the hash changes with the code the counters were taken on and not with its comments."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files:
+        text = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def measured_traffic(workload_name, record="sparse_decode_traffic.json"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources and this workload; else None."""
-    import hashlib
+    were taken on the current kernel code and this workload; else None."""
     path = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(path))
-        h = hashlib.sha256()
-        for f in rec["sources"]:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest() != rec["sources_sha256"] or rec["workload"] != workload_name:
+        if code_sha256(rec["sources"]) != rec["code_sha256"] or rec["workload"] != workload_name:
             return None
         return int(rec["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

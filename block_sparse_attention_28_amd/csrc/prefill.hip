@@ -22,13 +22,13 @@
 //   prefill_select_rows    64x64 LDS tiles, and one wave per row selecting
 //   prefill_attention    : 64 query rows per workgroup; each wave takes 32
 //                          rows and one 32-key half of every kept block, MFMA
-//                          v_mfma_f32_16x16x32_bf16.  S^T = K Q^T so that each
+//                          v_mfma_f32_32x32x16_bf16.  S^T = K Q^T so that each
 //                          lane holds one query row's probabilities in exactly
-//                          the operand layout of O^T = V^T P^T; K is staged in
-//                          LDS row-major, V transposed, both XOR-swizzled
-//                          against bank conflicts; the next kept block's K/V
-//                          are prefetched into registers while the current one
-//                          is computed, and the two key halves of each row are
+//                          the operand layout of O^T = V^T P^T; K and V tiles
+//                          go from HBM straight into double-buffered LDS
+//                          (XOR-swizzled against bank conflicts, V^T read with
+//                          transposing LDS reads) while the previous block is
+//                          computed, and the two key halves of each row are
 //                          merged once at the end.
 #include "seer_device.hpp"
 #include "seer_host.hpp"
