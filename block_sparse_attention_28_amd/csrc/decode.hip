@@ -11,8 +11,8 @@
 // The kernel bodies, and the description of their gfx950 mapping (LDS-direct
 // K/V tile loads, both products on v_mfma_f32_16x16x32_bf16 with the group's
 // query heads as the N dimension, log2-domain online softmax, per-split
-// (o, m, l) partials), are in decode_items.hpp, shared with the fused decode
-// step.  This file holds the launches: the split kernel, the log-sum-exp merge
+// (o, m, l) partials), are in decode_items.hpp, shared with the two-launch
+// decode step.  This file holds the launches: the split kernel, the log-sum-exp merge
 // of the splits, and the dense ground-truth form with its block masses.
 #include "decode_items.hpp"
 
@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void block_mass_split_kernel(c
 }
 
 // One (b, KV head) per workgroup: mass of unit u = mean over the group's heads
-// of 2^(log2-sum-exp of the unit - log2-sum-exp of the whole context).
+// of 2^(log2-sum-exp of the unit - log2-sum-exp of the whole context).  A
+// unit's log2-sum-exp is kept as one entry per 32-token slice (block_size / 32
+// of the 4 slots).
 template <int G>
 __global__ __launch_bounds__(256) void block_mass_kernel(const float *blk_lse, const float *lse, const int32_t *seqlens,
                                                          int Hq, int Hkv, int kv_capacity, int block_size, int nb_max,
@@ -74,13 +76,18 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const float *blk_lse, c
         float m = 0.f;
         if (u >= 0) {
             const float *x = blk_lse + ((int64_t)pair * (nb_max + 1) + u) * G * 4;
+            const int nslot = block_size / 32;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float w0 = x[h * 4], w1 = x[h * 4 + 1], w2 = x[h * 4 + 2], w3 = x[h * 4 + 3];
-                const float mx = fmaxf(fmaxf(w0, w1), fmaxf(w2, w3));
+                float w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = e < nslot ? x[h * 4 + e] : -INFINITY;
+                const float mx = fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3]));
                 if (mx == -INFINITY || lse2[h] == -INFINITY) continue;
-                const float t = mx + log2f(exp2f(w0 - mx) + exp2f(w1 - mx) + exp2f(w2 - mx) + exp2f(w3 - mx));
-                m += exp2f(t - lse2[h]);
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum += exp2f(w[e] - mx);
+                m += exp2f(mx + log2f(sum) - lse2[h]);
             }
             m *= 1.0f / (float)G;
         }

@@ -1,8 +1,8 @@
 // decode_items.hpp -- device bodies of the sparse-decode split and its merge.
 //
-// Used by the standalone kernels (decode.hip) and by the fused one-launch
-// decode step (step.hip); the Mem policy (seer_device.hpp) says how data
-// handed to another workgroup is written and read.
+// Used by the standalone kernels (decode.hip), the per-head form (heads.hip)
+// and the two-launch decode step (step.hip); the Mem policy (seer_device.hpp)
+// says how data handed to another workgroup is written and read.
 //
 // Operation ("SeerAttention-R: Sparse Attention Adaptation for Long
 // Reasoning", abstract): a decoding kernel that reads only the KV blocks the
@@ -11,15 +11,15 @@
 // tail is always attended: it holds the current token and has no pooled key
 // to be scored with.
 //
-// gfx950 design.  One workgroup (4 waves) per (split, KV head, sequence).  A
-// split owns a contiguous range of "units" (a kept block, or the tail).  For
-// every unit each wave takes a quarter of the block's tokens (32 or 16) and
-// does both products on v_mfma_f32_16x16x{32,16}_bf16 with the group's query
-// heads as the 16-wide N dimension (G <= 8 of them used):
-//   loads : the wave's K and V rows of the unit go straight from HBM into its
+// gfx950 design.  One workgroup (4 waves) per (split, KV head, sequence).  The
+// pair's "units" (the kept blocks, then the tail) are cut into 32-token
+// slices; a split owns a contiguous range of slices, dealt round-robin to its
+// waves.  For each slice a wave does both products on v_mfma_f32_16x16x32_bf16
+// with the group's query heads as the 16-wide N dimension (G <= 8 used):
+//   loads : the wave's K and V rows of the slice go straight from HBM into its
 //        LDS tiles (buffer_load ... lds, non-temporal, whole 256-byte rows per
-//        16 lanes; the unit's first row is a scalar offset, rows past the
-//        cache read as zero).  A lane's 16 bytes land at base + 16 lane, so the
+//        16 lanes; the slice's first row is a scalar offset, rows past the
+//        context re-read its last token).  A lane's 16 bytes land at base + 16 lane, so the
 //        bank-conflict swizzles below are a choice of source chunk per lane.
 //   QK : S^T = K Q^T, the K operand read from LDS (16-byte chunks XOR-swizzled
 //        by row), the bf16 query a register operand.  Lane (g4, n) gets head
@@ -35,8 +35,8 @@
 // At the end each wave's heads and then the 4 waves are combined, and the
 // split writes (unnormalised o, running max, running sum) per head -- or,
 // with a single split, the final normalised output directly.  A merge of the
-// splits by log-sum-exp follows (a second kernel, or later work items of the
-// fused step).
+// splits by log-sum-exp follows (a second kernel, or the pair's last split in
+// the two-launch step).
 #pragma once
 
 #include "seer_device.hpp"
@@ -89,7 +89,8 @@ __host__ __device__ inline int heads_union_words(int nb_max, int G, int k_max) {
 template <int D, int BS, int G>
 struct DecodeCfg {
     static constexpr int NT = 256, NW = 4;
-    static constexpr int TPW = BS / NW;  // tokens per wave per unit
+    static constexpr int TPW = 32;        // tokens of one slice: what a wave loads and attends at a time
+    static constexpr int SPB = BS / TPW;  // slices per unit (4 for 128-token blocks, 2 for 64)
 };
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -199,27 +200,30 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         nsel = GT ? kcap : (KL ? kept_n : Mem::ldi(a.n_sel + b * a.Hkv + g));
         nsel = nsel < 0 ? 0 : (nsel > kcap ? kcap : nsel);
     }
-    // Each unit is NW slices, one per wave (wave w always takes the unit's
-    // w-th quarter of tokens).  The S splits divide the pair's slices evenly, so
+    // Each unit is SPB slices of 32 tokens; slice i is tokens 32 (i % SPB) ..
+    // + 31 of unit i / SPB.  The S splits divide the pair's slices evenly, so
     // every split moves the same bytes to within one slice even when the units
     // do not divide by S; a unit at a split boundary is shared by two splits.
+    // Within a split, wave w takes the slices i = w (mod NW): with 128-token
+    // blocks always the unit's w-th quarter, with 64-token blocks half of
+    // block 2 r + w / 2.  Either way a wave has 16 KiB of K and V in flight.
+    constexpr int TPW = C::TPW, SPB = C::SPB;
     const int units = nsel + (tail > 0 ? 1 : 0);
-    const int64_t nslices = (int64_t)units * C::NW;
+    const int64_t nslices = (int64_t)units * SPB;
     const int i0 = (int)((split * nslices) / a.num_splits);  // this split's slices [i0, i1)
     const int i1 = (int)(((split + 1) * nslices) / a.num_splits);
-    // This wave's units: those whose slice u NW + wave lies in [i0, i1).
-    const int u0 = __builtin_amdgcn_readfirstlane((i0 - wave + C::NW - 1) / C::NW);
-    const int u1 = __builtin_amdgcn_readfirstlane((i1 - wave + C::NW - 1) / C::NW);
+    // This wave's rounds r: those whose slice r NW + wave lies in [i0, i1).
+    const int r0 = __builtin_amdgcn_readfirstlane((i0 - wave + C::NW - 1) / C::NW);
+    const int r1 = __builtin_amdgcn_readfirstlane((i1 - wave + C::NW - 1) / C::NW);
 
-    constexpr int TPW = C::TPW;   // tokens per wave per unit: 32 or 16
-    constexpr int NKT = TPW / 16;  // 16-token tiles per wave
+    constexpr int NKT = TPW / 16;  // 16-token tiles per slice
     constexpr int KS = D / 32;     // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;     // 16-wide d tiles of O^T
     constexpr int CPR = D / 8;     // 16-byte chunks per row
     constexpr int RPD = 64 / CPR;  // rows per 1 KiB LDS load
     constexpr int NDMA = TPW / RPD;
     constexpr int XM = CPR / 2 - 1;  // 32-byte chunk swizzle mask
-    static_assert(G <= 16 && (TPW == 16 || TPW == 32), "MFMA decode tile");
+    static_assert(G <= 16 && TPW == 32 && SPB * TPW == BS, "MFMA decode tile");
     const int g4 = lane >> 4, n = lane & 15;
 
     // Q operand: lane (g4, n) holds dims 8 g4 + 32 ks .. + 7 of head n (zero for n >= G).
@@ -264,8 +268,9 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
     float m_run = -INFINITY, l_part = 0.f;  // of head n
 
     int ids = 0, id0 = -(1 << 30);  // kept block ids of units [id0, id0 + 64), one per lane
-    for (int u = u0; u < u1; ++u) {
-        const int qq = wave;  // this wave's quarter (slice) of every unit
+    for (int r = r0; r < r1; ++r) {
+        const int sl = r * C::NW + wave;  // this wave's slice of the round
+        const int u = sl / SPB;           // its unit
         int tok0, cnt;
         uint32_t hmask = (1u << G) - 1u;  // heads that take this unit
         if (u < nsel) {
@@ -292,7 +297,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
         }
         tok0 = __builtin_amdgcn_readfirstlane(tok0);
         cnt = __builtin_amdgcn_readfirstlane(cnt);
-        const int wt0 = qq * TPW;  // first token of this slice inside its unit
+        const int wt0 = (sl % SPB) * TPW;  // first token of this slice inside its unit
         if constexpr (!GT) {
             if (wt0 >= cnt) continue;  // a slice of the tail past the context: nothing to attend
         }
@@ -373,10 +378,10 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
                 lsum += s[t][i];
             }
         l_part = l_part * alpha + lsum;
-        if constexpr (GT) {  // this wave's log2-sum-exp of the unit (its quarter of the tokens)
+        if constexpr (GT) {  // log2-sum-exp of the slice, entry sl % SPB of the unit's 4
             const float lw = sum_xor32(sum_xor16(lsum));
             if (g4 == 0 && n < G)
-                a.blk_lse[(((int64_t)(b * a.Hkv + g) * a.units_max + u) * G + n) * C::NW + wave] =
+                a.blk_lse[(((int64_t)(b * a.Hkv + g) * a.units_max + u) * G + n) * 4 + sl % SPB] =
                     lw > 0.f ? m_ref + log2f(lw) : -INFINITY;
         }
         if (__ballot(alpha != 1.0f)) {  // some head's maximum moved
@@ -384,44 +389,26 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         }
 
-        // P^T operands, high and low bf16 parts: k-slots 8 g4 + 4t + i <- token 16t + 4 g4 + i
-        // (k-slots 4 g4 + i for 16-token waves).
+        // P^T operands, high and low bf16 parts: k-slots 8 g4 + 4t + i <- token 16t + 4 g4 + i.
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V rows are in LDS
-        if constexpr (TPW == 32) {
-            bf16x8_t ph, pl;
+        bf16x8_t ph, pl;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const __bf16 hi = (__bf16)s[t][i];
-                    ph[4 * t + i] = hi;
-                    pl[4 * t + i] = (__bf16)(s[t][i] - (float)hi);
-                }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const char *p = vr0 + ((dt ^ tx) << 5);
-                const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
-                const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s *)(p + 16 * D * 2));
-                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, oacc[dt], 0, 0, 0);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, oacc[dt], 0, 0, 0);
-            }
-        } else {
-            v4s ph, pl;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const __bf16 hi = (__bf16)s[0][i];
-                ph[i] = __builtin_bit_cast(short, hi);
-                pl[i] = __builtin_bit_cast(short, (__bf16)(s[0][i] - (float)hi));
+                const __bf16 hi = (__bf16)s[t][i];
+                ph[4 * t + i] = hi;
+                pl[4 * t + i] = (__bf16)(s[t][i] - (float)hi);
             }
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const v4s vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s *)(vr0 + ((dt ^ tx) << 5)));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, ph, oacc[dt], 0, 0, 0);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pl, oacc[dt], 0, 0, 0);
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+            const char *p = vr0 + ((dt ^ tx) << 5);
+            const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+            const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s *)(p + 16 * D * 2));
+            const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, oacc[dt], 0, 0, 0);
         }
         // The next unit's loads overwrite the tile: keep them behind this unit's reads.
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)

@@ -68,13 +68,14 @@ __global__ __launch_bounds__(256) void mfma_32x32x16_kernel(float *sink, int ite
 }
 
 // One workgroup per (split, KV head, sequence), as the decode: the kept blocks
-// of the pair divided over the splits at quarter-block (per-wave) granularity.
+// of the pair cut into 32-token slices, divided over the splits, and dealt
+// round-robin to the waves.
 template <int BS>
 __global__ __launch_bounds__(256) void gather_kv_kernel(const uint16_t *k, const uint16_t *v, int64_t skv_b,
                                                         int64_t skv_h, int kv_capacity, const int32_t *block_idx,
                                                         int k_max, int nsel, int num_splits, int Hkv,
                                                         uint32_t *sink) {
-    constexpr int D = 128, TPW = BS / 4, NDMA = TPW / 4;  // 4 rows of 256 B per 1 KiB load
+    constexpr int D = 128, TPW = 32, SPB = BS / TPW, NDMA = TPW / 4;  // 4 rows of 256 B per 1 KiB load
     __shared__ __attribute__((aligned(16))) uint16_t kt[4][TPW * D], vt[4][TPW * D];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -83,17 +84,18 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(const uint16_t *k, const
     const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, region, 0x00020000);
     const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, region, 0x00020000);
     const int32_t *sel = block_idx + (int64_t)(b * Hkv + g) * k_max;
-    const int64_t ns = (int64_t)nsel * 4;
+    const int64_t ns = (int64_t)nsel * SPB;
     const int i0 = (int)((split * ns) / num_splits), i1 = (int)(((split + 1) * ns) / num_splits);
-    const int u0 = __builtin_amdgcn_readfirstlane((i0 - wave + 3) / 4);
-    const int u1 = __builtin_amdgcn_readfirstlane((i1 - wave + 3) / 4);
+    const int r0 = __builtin_amdgcn_readfirstlane((i0 - wave + 3) / 4);
+    const int r1 = __builtin_amdgcn_readfirstlane((i1 - wave + 3) / 4);
     const uint32_t lane_off = (uint32_t)(((lane / 16) * D + (lane % 16) * 8) * 2);
     char *kt_w = reinterpret_cast<char *>(kt[wave]), *vt_w = reinterpret_cast<char *>(vt[wave]);
     const int nb = kv_capacity / BS;
-    for (int u = u0; u < u1; ++u) {
-        int blk = __builtin_amdgcn_readfirstlane(sel[u]);
+    for (int r = r0; r < r1; ++r) {
+        const int sl = 4 * r + wave;  // < ns, so its block sl / SPB < nsel
+        int blk = __builtin_amdgcn_readfirstlane(sel[sl / SPB]);
         blk = blk < 0 ? 0 : (blk >= nb ? nb - 1 : blk);  // stays inside the cache
-        const uint32_t soff = (uint32_t)(blk * BS + wave * TPW) * D * 2u;
+        const uint32_t soff = (uint32_t)(blk * BS + (sl % SPB) * TPW) * D * 2u;
 #pragma unroll
         for (int q = 0; q < NDMA; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)(kt_w + q * 1024), 16,
