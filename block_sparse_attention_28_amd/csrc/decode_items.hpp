@@ -106,14 +106,15 @@ __device__ __forceinline__ void store_out(void *out, int dtype, int64_t i, float
         static_cast<uint16_t *>(out)[i] = f32_to_bf16(x);
 }
 
-// LDS of one split: each wave's K and V rows of the current unit, and the
-// per-wave partial results combined at the end.
+// LDS of one split: each wave's K and V rows of the current slice, and the
+// per-wave partial results combined at the end (each wave's o [G][D] in its
+// own K tile, which is free once its slices are done).
 template <int D, int BS, int G>
 struct DecodeSmem {
     using C = DecodeCfg<D, BS, G>;
     __attribute__((aligned(16))) uint16_t kt[C::NW][C::TPW * D];
     __attribute__((aligned(16))) uint16_t vt[C::NW][C::TPW * D];
-    float o[C::NW][G][D];
+    static_assert(G * D * sizeof(float) <= C::TPW * D * sizeof(uint16_t), "a wave's o fits its K tile");
     float m[C::NW][G], l[C::NW][G];
     int n_union;  // per-head form: size of the group's union of kept blocks
 };
@@ -134,7 +135,8 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
                                                   const int32_t *kept = nullptr, int kept_n = 0) {
     using C = DecodeCfg<D, BS, G>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    auto &sm_o = sm.o;
+    // Wave w's per-head o, [G][D] floats in its own K tile (used there only after its slices).
+    auto sm_o = [&](int w) { return reinterpret_cast<float (*)[D]>(sm.kt[w]); };
     auto &sm_m = sm.m;
     auto &sm_l = sm.l;
 
@@ -422,7 +424,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm_o[wave][n][16 * dt + 4 * g4 + i] = oacc[dt][i];
+            for (int i = 0; i < 4; ++i) sm_o(wave)[n][16 * dt + 4 * g4 + i] = oacc[dt][i];
         if (g4 == 0) {
             sm_m[wave][n] = m_run;
             sm_l[wave][n] = l_tot;
@@ -441,7 +443,7 @@ __device__ __forceinline__ void decode_split_item(const DecodeArgs &a, int split
 #pragma unroll
         for (int w = 0; w < C::NW; ++w) {
             const float f = fast_exp2(sm_m[w][h] - Mref);
-            O = fmaf(sm_o[w][h][e], f, O);
+            O = fmaf(sm_o(w)[h][e], f, O);
             Ls = fmaf(sm_l[w][h], f, Ls);
         }
         const int hq = g * G + h;
