@@ -152,7 +152,33 @@ def graph_step_us(plan, layers, steps, w, args):
         graphs[s % R].replay()
     e1.record()
     torch.cuda.synchronize()
-    return round(e0.elapsed_time(e1) * 1e3 / n, 2)
+    one = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+    # Four layers' steps in one graph: each replay's own launch cost is shared by four steps.
+    G = min(4, R)
+    qs = [torch.empty_like(g_q) for _ in range(G)]
+    for l in range(G):
+        qs[l].copy_(steps[l]["q"])
+    g_sl.copy_(steps[0]["seqlens"])
+    torch.cuda.synchronize()
+    g4 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g4):
+        for l in range(G):
+            c = layers[l].cache
+            plan.step(qs[l], c["k"], c["v"], g_sl, layers[l].kpool, c["wq"], c["wk"], mode=mode)
+    c = layers[G - 1].cache
+    plan.step(qs[G - 1], c["k"], c["v"], g_sl, layers[G - 1].kpool, c["wq"], c["wk"], mode=mode)
+    torch.cuda.synchronize()
+    ref = plan.out.clone()
+    g4.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(ref, plan.out), "multi-step graph replay differs from the eager step"
+    reps = max(1, n // G)
+    e0.record()
+    for _ in range(reps):
+        g4.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"one_step_per_graph": one, "four_steps_per_graph": round(e0.elapsed_time(e1) * 1e3 / (reps * G), 2)}
 
 
 def dense_decode_us(w, lay, base_L, dev):
