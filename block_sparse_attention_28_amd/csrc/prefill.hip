@@ -522,22 +522,34 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // 32 kh + 8 a + 4 hl + b of query row qtok.  The even and odd k-steps
     // accumulate separately (two independent MFMA chains instead of one chain
     // of 8) and are added at the end.
-    auto scores = [&](f32x16_t &s, const char *kb) {
+    // kread: the K operand of this wave's 32 keys for every k-step (offsets masked
+    // to the buffer's 16 KiB, which they never exceed: the compiler then sees that
+    // the reads cannot touch a buffer being loaded).  smma: the MFMAs.
+    const int krow_off = (32 * kh + n) * (D * 2);
+    auto kread = [&](bf16x8_t (&ka)[KS], const char *kb) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            ka[ks] = *reinterpret_cast<const bf16x8_t *>(
+                kb + ((krow_off + (((2 * ks + hl) ^ (n & 15)) << 4)) & (KBYTES - 1)));
+    };
+    auto smma = [&](f32x16_t &s, const bf16x8_t (&ka)[KS]) {
         f32x16_t s1;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             s[e] = 0.f;
             s1[e] = 0.f;
         }
-        const char *krow_lds = kb + (32 * kh + n) * (D * 2);
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
-            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((2 * ks + hl) ^ (n & 15)) << 4));
-            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(krow_lds + (((2 * ks + 2 + hl) ^ (n & 15)) << 4));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[ks], s, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[ks + 1], s1, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], s, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks + 1], qop[ks + 1], s1, 0, 0, 0);
         }
         s += s1;
+    };
+    auto scores = [&](f32x16_t &s, const char *kb) {
+        bf16x8_t ka[KS];
+        kread(ka, kb);
+        smma(s, ka);
     };
     // Causal / length masks: only the diagonal block and a partial last block need them.
     auto is_edge = [&](int it) {
@@ -715,23 +727,49 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         }
     }
     if constexpr (GT) {
-        // Second sweep: each block's share of every row's softmax, averaged over the block's rows.
+        // Second sweep: each block's share of every row's softmax, averaged over
+        // the block's rows.  The K tiles rotate through all four tile buffers,
+        // three blocks ahead of the one being scored, with one barrier per block;
+        // the block's sum over the four waves goes through a double-buffered slot
+        // and is written out by thread 0 after the next barrier.
         __shared__ float row_lse2[64];
-        __shared__ float red[4];
+        __shared__ float red[2][4];
         if (kh == 0 && hl == 0) row_lse2[32 * rh + n] = lse2;
-        __syncthreads();
+        __syncthreads();  // also: the exchange area in the K buffers is free
         lse2 = row_lse2[32 * rh + n];
         const int rows_i = L - i * kPBS < kPBS ? L - i * kPBS : kPBS;
         float *mrow = mass + row * nb;
         for (int jj = i + 1 + tid; jj < nb; jj += 256) mrow[jj] = 0.f;
-        for (int jb = 0; jb <= i; ++jb) {
-            const int k0 = jb * kPBS;
-            __syncthreads();  // previous readers of the K buffer and red are done
-            dma(jb, kbuf0, krs, kdv);
-            loads_done();
-            __syncthreads();
+        auto block_mass_out = [&](int jb) {
+            if (tid == 0) mrow[jb] = (red[jb & 1][0] + red[jb & 1][1] + red[jb & 1][2] + red[jb & 1][3]) / (float)rows_i;
+        };
+        dma(0, kbuf0, krs, kdv);
+        if (i >= 1) dma(1, kbuf1, krs, kdv);
+        if (i >= 2) dma(2, vbuf0, krs, kdv);
+        auto sweep = [&](auto par, int jb) {
+            constexpr int P = decltype(par)::value;
+            char *const cur = P == 0 ? kbuf0 : (P == 1 ? kbuf1 : (P == 2 ? vbuf0 : vbuf1));
+            char *const nxt3 = P == 0 ? vbuf1 : (P == 1 ? kbuf0 : (P == 2 ? kbuf1 : vbuf0));  // block jb - 1's
+            // This wave's loads of block jb have landed once at most its loads of
+            // the later blocks (up to two) are still in flight; then a plain
+            // s_barrier (a __syncthreads would wait for those too).
+            const int later = i - jb < 2 ? i - jb : 2;
+            if (later == 2)
+                __builtin_amdgcn_s_waitcnt((2 * DMA_PER_WAVE) | 0x0070);  // vmcnt(8), lgkmcnt(0)
+            else if (later == 1)
+                __builtin_amdgcn_s_waitcnt(DMA_PER_WAVE | 0x0070);
+            else
+                __builtin_amdgcn_s_waitcnt(0x0070);
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            __asm__ volatile("" ::: "memory");
+            if (jb > 0) block_mass_out(jb - 1);
+            bf16x8_t ka[KS];
+            kread(ka, cur);
+            if (jb + 3 <= i) dma(jb + 3, nxt3, krs, kdv);  // after this block's K reads
             f32x16_t s;
-            scores(s, kbuf0);
+            smma(s, ka);
+            const int k0 = jb * kPBS;
             float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -740,10 +778,26 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                 psum += live ? fast_exp2(s[e] * scale_log2 - lse2) : 0.f;
             }
             psum = wave_sum(psum);
-            if (lane == 0) red[wave] = psum;
-            __syncthreads();
-            if (tid == 0) mrow[jb] = (red[0] + red[1] + red[2] + red[3]) / (float)rows_i;
+            if (lane == 0) red[jb & 1][wave] = psum;
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        for (int jb = 0; jb <= i; jb += 4) {
+            sweep(I0{}, jb);
+            if (jb + 1 > i) break;
+            sweep(I1{}, jb + 1);
+            if (jb + 2 > i) break;
+            sweep(I2{}, jb + 2);
+            if (jb + 3 > i) break;
+            sweep(I3{}, jb + 3);
         }
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        block_mass_out(i);
     }
 }
 
