@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0 = skip)")
     ap.add_argument("--cpu-sequences", type=int, default=2)
     ap.add_argument("--prefill-steps", type=int, default=9, help="block-sparse prefill timing: gated and given-block call pairs (0 = skip)")
-    ap.add_argument("--mode", default="calls", choices=("gate_select", "calls", "fused"),
+    ap.add_argument("--mode", default="step", choices=("gate_select", "calls", "step"),
                     help="form of the timed step (the others are timed briefly for context)")
     ap.add_argument("--mode-steps", type=int, default=16, help="steps per form in the context timing (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=16, help="HIP-graph replays timed (0 = skip)")
@@ -106,21 +106,16 @@ def decode_bytes(w, seqlens_host):
     return kv, kv + q_out + ids
 
 
-def gate_bytes(w, seqlens_host):
-    """Algorithmic bytes of the gate and selection: fp32 pooled keys of the complete blocks,
-    the query, both gate weight matrices, and the scores written and read back."""
-    kp = sum(w.Hkv * (L // w.bs) * w.d * 4 for L in seqlens_host)
-    q = w.B * w.Hq * w.d * 2
-    wts = 2 * w.Hkv * w.gate_dim * w.d * 2
-    sc = 2 * sum(w.Hkv * (L // w.bs) * 4 for L in seqlens_host)
-    return kp + q + wts + sc
+def score_bytes(w, seqlens_host):
+    """Gate scores the selection reads: one fp32 per complete block and (b, KV head)."""
+    return sum(w.Hkv * (L // w.bs) * 4 for L in seqlens_host)
 
 
 def graph_step_us(plan, layers, steps, w, args):
     """The step in its timed form (gate, select, decode) captured once per layer as a HIP graph,
     then replayed.  Each replay's output is checked against the eager step's."""
     R = len(layers)
-    mode = "gate_select" if args.mode == "gate_select" else "calls"
+    mode = args.mode
     g_q = torch.empty_like(steps[0]["q"])
     g_sl = torch.empty_like(steps[0]["seqlens"])
     graphs = []
@@ -333,32 +328,35 @@ def time_launches(fn, n, warm=3):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
-def decode_workload_context(w, dev, layers=3, steps=16):
-    """Another decode workload in the timed form (three calls) on rotated layers: the step and its
-    seer_sparse_decode launch (split + merge), with that launch's algorithmic bytes."""
+def decode_workload_context(w, dev, mode, layers=3, steps=16):
+    """Another decode workload on rotated layers: the step in the timed form, the step as three
+    calls, and the seer_sparse_decode launch (split + merge) with its algorithmic bytes."""
     lay = [Layer(w, l, 0, dev) for l in range(layers)]
     base_L = lay[0].cache["seqlens"].cpu().to(torch.int64)
     shape = pipeline.DecodeShape(w.B, w.Hq, w.Hkv, w.d, w.bs, w.budget, lay[0].nb_max, w.gate_dim)
     plan = pipeline.DecodePlan(shape, dev)
-    calls = []
+    calls, timed = [], []
     for l, ly in enumerate(lay):
         ub, uj = pipeline.full_pool_lists(base_L, w.bs, dev)
         plan.pool(ly.cache["k"], ly.kpool, ub, uj)
-        calls.append(plan.bind_step(inputs.decode_query(w, l, dev), ly.cache["k"], ly.cache["v"], ly.cache["seqlens"],
-                                    ly.kpool, ly.cache["wq"], ly.cache["wk"], mode="calls"))
+        args = (inputs.decode_query(w, l, dev), ly.cache["k"], ly.cache["v"], ly.cache["seqlens"], ly.kpool,
+                ly.cache["wq"], ly.cache["wk"])
+        calls.append(plan.bind_step(*args, mode="calls"))
+        timed.append(plan.bind_step(*args, mode=mode))
 
-    def step(i):
-        for c in calls[i % layers]:
+    def step(i, form):
+        for c in form[i % layers]:
             c()
-    us_step = time_launches(step, steps)
+    us_step = time_launches(lambda i: step(i, timed), steps)
+    us_calls = time_launches(lambda i: step(i, calls), steps)
     us_dec = time_launches(lambda i: calls[i % layers][-1](), steps)
     _, alg = decode_bytes(w, base_L.tolist())
-    out = {"workload": w.name, "us_step": round(us_step, 2), "us_decode_launch": round(us_dec, 2),
-           "bytes_per_launch": int(alg), "num_splits": plan.num_splits}
+    out = {"workload": w.name, "step_form": mode, "us_step": round(us_step, 2), "us_step_calls": round(us_calls, 2),
+           "us_decode_launch": round(us_dec, 2), "bytes_per_launch": int(alg), "num_splits": plan.num_splits}
     if alg > 10_000_000:  # the tiny workload is latency-bound: microseconds only
         gbps = alg / (us_dec * 1e-6) / 1e9
         out.update({"achieved_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
-    del lay, plan, calls
+    del lay, plan, calls, timed
     torch.cuda.empty_cache()
     return out
 
@@ -437,7 +435,7 @@ def main():
         c = lay.cache
         st["pool"] = seer.seer_pool_k_blocks(c["k"], *st["upd"], lay.kpool, w.bs, bind=True) if st["upd"] else None
         st["calls"] = {m: plan.bind_step(st["q"], c["k"], c["v"], st["seqlens"], lay.kpool, c["wq"], c["wk"], mode=m)
-                       for m in ("calls", "gate_select", "fused")}
+                       for m in ("calls", "gate_select", "step")}
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -455,7 +453,7 @@ def main():
             call()
         if events:
             ev[s][1].record(stream)
-        calls[-1]()  # the decode (or the whole fused step)
+        calls[-1]()  # the decode launch (split + merge; with the selection in the step form)
         if events:
             ev[s][2].record(stream)
 
@@ -486,20 +484,25 @@ def main():
     mean_alg = sum(b[1] for b in kv_bytes) / K
     value = mean_kv / (ms_per_step * 1e-3) / 1e9
     dom_us = sum(ev[s][1].elapsed_time(ev[s][2]) * 1e3 for s in range(W, total)) / K
-    if mode == "fused":
-        # one launch does the whole step: its algorithmic bytes include the gate's reads
-        dom_bytes = mean_alg + gate_bytes(w, steps[W]["L"])
-        dom_name = "seer_decode_step (gate kernel, then select + split decode + merge kernel)"
+    if mode == "step":
+        # the selection runs in the decode kernel: its launch also reads the pair's gate scores
+        dom_bytes = mean_alg + score_bytes(w, steps[W]["L"])
+        dom_name = "seer_select_sparse_decode (select + split decode kernel, LSE merge kernel)"
+        traffic_record = "select_sparse_decode_traffic.json"
     else:
         dom_bytes = mean_alg
         dom_name = "seer_sparse_decode (split kernel + LSE merge kernel)"
+        traffic_record = "sparse_decode_traffic.json"
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    # The decode launch of the three-call form (split + merge kernels alone), on the same steps.
+    dec_calls = [steps[s]["calls"]["calls"][-1] for s in range(W, total)]
+    us_dec_calls = time_launches(lambda i: dec_calls[i % len(dec_calls)](), len(dec_calls))
     kept = min(w.k_max, int(base_L.min()) // w.bs)
     ncb = int(base_L.min()) // w.bs
 
     # Context: the other step forms on the same layers, and the step replayed as a HIP graph.
     modes_us = {}
-    for m in ("calls", "gate_select", "fused"):
+    for m in ("calls", "gate_select", "step"):
         if args.mode_steps <= 0:
             break
         n = min(args.mode_steps, total)
@@ -546,7 +549,7 @@ def main():
         "graph_step_us": graph_us,
         "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name) if mode != "fused" else None,
+                     "traffic": measured_traffic(w.name, traffic_record) if mode != "gate_select" else None,
                      "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
         "dense_decode": dense,
         "ground_truth": gt,
@@ -554,6 +557,11 @@ def main():
         "per_head_selection": ph,
         "ceilings": ceil,
     }
+    line["roofline"]["seer_sparse_decode_launch"] = {
+        "us": round(us_dec_calls, 2), "bytes": int(mean_alg),
+        "frac": round(mean_alg / (us_dec_calls * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "traffic": measured_traffic(w.name, "sparse_decode_traffic.json"),
+        "note": "split + merge kernels of the three-call form (no selection inside), same steps"}
     if ceil:
         line["roofline"]["frac_of_gather_read"] = round(achieved / ceil["gather_read"]["GBps"], 4)
     if args.cpu_seconds > 0:
@@ -561,7 +569,8 @@ def main():
     del layers, steps, plan
     torch.cuda.empty_cache()
     if args.other:
-        line["other_workloads"] = [decode_workload_context(ow, dev) for ow in (DECODE_L32K, RAGGED_DECODE, TINY_DECODE)]
+        line["other_workloads"] = [decode_workload_context(ow, dev, mode)
+                                   for ow in (DECODE_L32K, RAGGED_DECODE, TINY_DECODE)]
     if args.prefill_steps > 0:
         line["secondary_path"] = bench_prefill(args.prefill_steps, dev, ceil)
     print(json.dumps(line), flush=True)

@@ -48,8 +48,7 @@ class DecodePlan:
         dws = seer.seer_sparse_decode_workspace_size(s.B, s.Hq, s.Hkv, s.d, s.k_max, s.bs, self.num_splits)
         self.decode_ws = torch.empty((max(dws, 16) + 3) // 4, dtype=torch.float32, device=dev)
         sws = seer.seer_decode_step_workspace_size(s.B, s.Hq, s.Hkv, s.d, s.k_max, s.bs, self.num_splits)
-        # zero-filled once: the step's merge counters return to zero after every launch
-        self.step_ws = torch.zeros((max(sws, 16) + 3) // 4, dtype=torch.float32, device=dev)
+        self.step_ws = torch.empty((max(sws, 16) + 3) // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((s.B, s.Hq, s.d), dtype=out_dtype, device=dev)
         self.lse = torch.empty((s.B, s.Hq), dtype=torch.float32, device=dev)
 
@@ -76,11 +75,10 @@ class DecodePlan:
     def step(self, q, k, v, seqlens, kpool, wq, wk, stream=None, mode: str = "calls"):
         """Gate, select and sparse-decode one step; returns (out, lse) views of the plan's buffers.
 
-        mode "calls" (the default, the fastest form measured): seer_gate_scores, seer_select_blocks,
-        seer_sparse_decode; "gate_select": seer_gate_select then seer_sparse_decode;
-        "fused": seer_decode_step (gate, then select + decode + merge in one launch), bit-for-bit the
-        "calls" results."""
-        if mode == "fused":
+        mode "calls": seer_gate_scores, seer_select_blocks, seer_sparse_decode; "gate_select":
+        seer_gate_select then seer_sparse_decode; "step": seer_decode_step (the gate, then select +
+        split decode in one launch, then the merge).  All three give the "calls" results bit for bit."""
+        if mode == "step":
             s = self.shape
             seer.seer_decode_step(q, k, v, seqlens, kpool, wq, wk, s.bs, s.budget, self.gate_scale,
                                   self.softmax_scale, self.scores, self.block_idx, self.n_sel, self.out, self.lse,
@@ -100,10 +98,14 @@ class DecodePlan:
         """The launches of one step (as in step()) with their arguments converted once:
         a list of callables, each launching one library call again."""
         s = self.shape
-        if mode == "fused":
-            return [seer.seer_decode_step(q, k, v, seqlens, kpool, wq, wk, s.bs, s.budget, self.gate_scale,
-                                          self.softmax_scale, self.scores, self.block_idx, self.n_sel, self.out,
-                                          self.lse, self.step_ws, self.num_splits, stream=stream, bind=True)]
+        if mode == "step":
+            # seer_decode_step's launches as two calls, so that the last one (select + split decode, merge)
+            # can be timed on its own
+            return [seer.seer_gate_scores(q, wq, wk, kpool, seqlens, s.bs, self.gate_scale, self.scores,
+                                          stream=stream, bind=True),
+                    seer.seer_select_sparse_decode(q, k, v, seqlens, self.scores, s.bs, s.budget, self.softmax_scale,
+                                                   self.block_idx, self.n_sel, self.out, self.lse, self.step_ws,
+                                                   self.num_splits, stream=stream, bind=True)]
         if mode == "calls":
             calls = [seer.seer_gate_scores(q, wq, wk, kpool, seqlens, s.bs, self.gate_scale, self.scores,
                                            stream=stream, bind=True),

@@ -65,6 +65,8 @@ SIGNATURES = {
     "seer_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "seer_decode_step": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _I, _F, _P, _I, _I, _I, _I,
                               _I, _I, _I, _F, _I, _P, _P, _P, _P, _SZ, _P, _I, _P, _P]),
+    "seer_select_sparse_decode": (_I, [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _I, _F, _I, _P, _P, _P, _SZ, _P, _I, _P, _P]),
     "seer_block_sparse_prefill_kmax_row": (_I, [_I, _I, _I, _I]),
     "seer_block_sparse_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "seer_block_sparse_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _F, _I, _I, _P, _P, _I, _I, _F,
@@ -393,7 +395,8 @@ def seer_decode_step_workspace_size(B: int, Hq: int, Hkv: int, d: int, k_max: in
 def seer_decode_step(q, k, v, seqlens, kpool, wq, wk, block_size: int, budget_tokens: int, gate_scale: float,
                      softmax_scale: float, scores, block_idx, n_sel, out, lse=None, workspace=None,
                      num_splits: int = 0, stream=None, bind: bool = False):
-    """Gate + select + sparse decode in one launch (same results as the three separate calls)."""
+    """Gate + select + sparse decode in three launches: the gate, select + split decode, the merge
+    (same results as the three separate calls)."""
     _bits(q), _bits(k), _bits(v), _bits(wq), _bits(wk)
     B, Hq, d = q.shape
     _, Hkv, cap, _ = k.shape
@@ -407,4 +410,24 @@ def seer_decode_step(q, k, v, seqlens, kpool, wq, wk, block_size: int, budget_to
         k.stride(2), cap, _ptr(seqlens), _ptr(wq), _ptr(wk), dg, float(gate_scale), _ptr(kpool), kpool.shape[2], B,
         Hq, Hkv, d, block_size, int(budget_tokens), float(softmax_scale), int(num_splits), _ptr(scores),
         _ptr(block_idx) if k_max else None, _ptr(n_sel), _ptr(workspace), ws_bytes, _ptr(out), out_dtype, _ptr(lse),
+        _stream(stream), bind=bind)
+
+
+def seer_select_sparse_decode(q, k, v, seqlens, scores, block_size: int, budget_tokens: int, softmax_scale: float,
+                              block_idx, n_sel, out, lse=None, workspace=None, num_splits: int = 0, stream=None,
+                              bind: bool = False):
+    """From given gate scores [B, Hkv, nb_max]: the selection inside the decode kernel, then the merge
+    (seer_decode_step's last two launches; same results as seer_select_blocks + seer_sparse_decode)."""
+    _bits(q), _bits(k), _bits(v)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    assert k.stride() == v.stride() and out.is_contiguous() and scores.is_contiguous()
+    out_dtype = SEER_OUT_F32 if out.dtype == torch.float32 else SEER_OUT_BF16
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    k_max = budget_tokens // block_size
+    return _call(
+        "seer_select_sparse_decode", _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        k.stride(2), cap, _ptr(seqlens), _ptr(scores), scores.shape[2], B, Hq, Hkv, d, block_size,
+        int(budget_tokens), float(softmax_scale), int(num_splits), _ptr(block_idx) if k_max else None, _ptr(n_sel),
+        _ptr(workspace) if workspace is not None else None, ws_bytes, _ptr(out), out_dtype, _ptr(lse),
         _stream(stream), bind=bind)

@@ -299,22 +299,38 @@ int seer_decode_block_mass(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
 
 /*
  * One whole decode step: the gate scores, the token-budget selection and the
- * sparse decode with its merge, in two kernel launches instead of four: the
- * gate scores, then one kernel whose workgroups select their (b, KV head)'s
- * blocks in LDS, decode their split and, the last split of each (b, KV head),
- * merge the splits.  The results equal those of seer_gate_scores +
- * seer_select_blocks + seer_sparse_decode with the same arguments bit for bit.
+ * sparse decode with its merge, in three kernel launches instead of four: the
+ * gate scores; one kernel whose workgroups select their (b, KV head)'s blocks
+ * in LDS and decode their split; the merge of the splits (none with a single
+ * split).  The results equal those of seer_gate_scores + seer_select_blocks +
+ * seer_sparse_decode with the same arguments bit for bit.
  *   arguments as in the three calls above; scores [B][Hkv][nb_max],
  *   block_idx [B][Hkv][budget_tokens / block_size] and n_sel [B][Hkv] are
  *   written as those calls write them.
- *   workspace >= seer_decode_step_workspace_size(...) bytes: one counter per
- *              (b, KV head), then the split partials.  It must be zero-filled
- *              before its first use; every call leaves the counters at zero
- *              again.  Calls sharing a workspace must be ordered on one stream.
+ *   workspace >= seer_decode_step_workspace_size(...) bytes (the split
+ *              partials, as seer_sparse_decode's; may be null when that is 0).
+ *              Calls sharing a workspace must be ordered on one stream.
  * nb_max <= 16128; B * Hkv <= 65535.
  */
 size_t seer_decode_step_workspace_size(int B, int Hq, int Hkv, int d, int k_max, int block_size,
                                        int num_splits);
+
+/*
+ * The second and third launches of seer_decode_step on their own: from given
+ * gate scores, the token-budget selection (in the decode kernel's LDS) and the
+ * sparse decode, then the merge of the splits.  Results equal
+ * seer_select_blocks + seer_sparse_decode with the same arguments bit for bit.
+ *   scores [B][Hkv][nb_max] fp32 (as seer_gate_scores writes them; entries past
+ *   a sequence's complete blocks are not read); the other arguments as in
+ *   seer_decode_step, workspace as seer_sparse_decode_workspace_size reports.
+ */
+int seer_select_sparse_decode(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
+                              const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
+                              int kv_capacity, const int32_t *seqlens, const float *scores, int nb_max,
+                              int B, int Hq, int Hkv, int d, int block_size, int budget_tokens,
+                              float softmax_scale, int num_splits, int32_t *block_idx, int32_t *n_sel,
+                              void *workspace, size_t workspace_bytes, void *out, int out_dtype, float *lse,
+                              hipStream_t stream);
 int seer_decode_step(const seer_bf16 *q, int64_t sq_b, int64_t sq_h,
                      const seer_bf16 *k, const seer_bf16 *v, int64_t skv_b, int64_t skv_h, int64_t skv_t,
                      int kv_capacity, const int32_t *seqlens,

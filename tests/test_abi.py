@@ -102,6 +102,7 @@ def test_decode_calls_reject_a_non_positive_softmax_scale(lib, scale):
           C.c_float(0.1), FAKE, 16, 2, 32, 8, 128, 64, 256, C.c_float(scale), 1, FAKE, FAKE, FAKE, FAKE, 1 << 30,
           FAKE, 0, NULL, NULL]
     assert lib.seer_decode_step(*st) == -1
+    assert lib.seer_select_sparse_decode(*select_decode_args(scale=scale)) == -1
     pf = [FAKE, FAKE, FAKE, 1, 2, 1024, 128, 64, NULL, NULL, 128, C.c_float(0.1), 1, 10, FAKE, FAKE, 4, 1,
           C.c_float(scale), NULL, 0, FAKE, NULL, NULL]
     assert lib.seer_block_sparse_prefill(*pf) == -1
@@ -182,6 +183,21 @@ def test_other_calls_reject_bad_arguments(lib):
     assert lib.seer_gate_select(*gs) == -1
     gs[17], gs[12], gs[1], gs[2] = FAKE, 96, 32 * 96, 96
     assert lib.seer_gate_select(*gs) == -2
+
+
+def select_decode_args(scale=0.088, scores=FAKE, nb_max=16, splits=1):
+    """seer_select_sparse_decode arguments of a valid call (the pointers are never dereferenced:
+    every test changes one argument so that validation fails before a launch)."""
+    return [FAKE, 32 * 128, 128, FAKE, FAKE, 8 * 1024 * 128, 1024 * 128, 128, 1024, FAKE, scores, nb_max, 2, 32, 8,
+            128, 64, 256, C.c_float(scale), splits, FAKE, FAKE, FAKE, 1 << 30, FAKE, 0, NULL, NULL]
+
+
+def test_select_sparse_decode_rejects_bad_arguments(lib):
+    assert lib.seer_select_sparse_decode(*select_decode_args(scores=NULL)) == -1
+    assert lib.seer_select_sparse_decode(*select_decode_args(nb_max=20000)) == -2  # keys exceed the LDS buffer
+    a = select_decode_args(splits=4)
+    a[22] = NULL  # partials needed, no workspace
+    assert lib.seer_select_sparse_decode(*a) == -3
 
 
 def test_noalloc_decode_rejects_partials_beyond_its_scratch(lib):

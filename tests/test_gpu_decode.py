@@ -28,15 +28,15 @@ def _gpu():
     seer.load()
 
 
-STEP_FORMS = ["calls", "gate_select", "fused"]
+STEP_FORMS = ["calls", "gate_select", "step"]
 
 
 @pytest.mark.parametrize("mode", STEP_FORMS)
 @pytest.mark.parametrize("splits", [0, 1, 2, 5])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_tiny_workload_full(splits, out_dtype, mode):
-    """Every form of the step (the three calls, the one-launch gate + select, the fused persistent
-    launch) against the oracle, not only against each other."""
+    """Every form of the step (the three calls, the one-launch gate + select, seer_decode_step)
+    against the oracle, not only against each other."""
     run = build_and_run(TINY_DECODE, num_splits=splits, out_dtype=out_dtype, mode=mode)
     ref = oracle_sequence(run, 0)
     st = check_sequence(run, 0, ref)
@@ -153,41 +153,57 @@ def test_select_exact_with_ties(nc, k):
             np.testing.assert_array_equal(idx[b, h, :len(ref)].cpu().numpy(), ref)
 
 
-FUSED_CASES = [TINY_DECODE, DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE,
-               DecodeWorkload(name="fused_tail_g2_d64", B=3, Hq=8, Hkv=4, d=64, bs=64, budget=384, seed=31,
+STEP_CASES = [TINY_DECODE, DECODE_L32K, DECODE_L64K_S90, RAGGED_DECODE,
+               DecodeWorkload(name="step_tail_g2_d64", B=3, Hq=8, Hkv=4, d=64, bs=64, budget=384, seed=31,
                               L_range=(100, 3000)),
-               DecodeWorkload(name="fused_empty", B=2, Hq=4, Hkv=1, d=128, bs=64, budget=0, seed=32, L=256)]
+               DecodeWorkload(name="step_empty", B=2, Hq=4, Hkv=1, d=128, bs=64, budget=0, seed=32, L=256)]
 
 
-def assert_same_step(fused, sep, what):
-    """The two-launch step against the separate calls: every output bit for bit."""
-    for n, a, b in zip(("scores", "block_idx", "n_sel", "out", "lse"), fused, sep):
-        assert torch.equal(a, b), f"{what}: {n} differs between the fused and the separate path"
+def assert_same_step(step, sep, what):
+    """seer_decode_step against the separate calls: every output bit for bit."""
+    for n, a, b in zip(("scores", "block_idx", "n_sel", "out", "lse"), step, sep):
+        assert torch.equal(a, b), f"{what}: {n} differs between seer_decode_step and the separate calls"
 
 
-@pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
-def test_fused_step_equals_separate_calls(w):
-    """seer_decode_step (gate launch, then select + decode + merge in one launch) against gate +
-    select + decode launched separately, twice in a row on one workspace (its counters must be
-    back at zero after each launch)."""
-    run = build_and_run(w, mode="fused")
+@pytest.mark.parametrize("w", STEP_CASES, ids=lambda w: w.name)
+def test_decode_step_equals_separate_calls(w):
+    """seer_decode_step (the gate, select + split decode in one launch, the merge) against gate +
+    select + decode launched separately, twice in a row on one workspace."""
+    run = build_and_run(w, mode="step")
     p = run.plan
-    fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    got = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(run.q, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"],
            run.cache["wk"], mode="calls")
     torch.cuda.synchronize()
     sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
-    assert_same_step(fused, sep, w.name)
+    assert_same_step(got, sep, w.name)
     q2 = inputs.decode_query(w, 1, "cuda")
     p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
-           mode="fused")
+           mode="step")
     torch.cuda.synchronize()
-    fused2 = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    got2 = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(q2, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"],
            mode="calls")
     torch.cuda.synchronize()
-    assert_same_step(fused2, [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], w.name + " #2")
-    assert torch.all(p.step_ws.view(torch.int32)[:w.B * w.Hkv] == 0), "step counters not back at zero"
+    assert_same_step(got2, [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], w.name + " #2")
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=lambda w: w.name)
+def test_select_sparse_decode_equals_separate_calls(w):
+    """seer_gate_scores + seer_select_sparse_decode (seer_decode_step's launches as two calls, the
+    form the benchmark times) against the separate calls, bit for bit; outputs cleared first."""
+    run = build_and_run(w, mode="calls")
+    p, c = run.plan, run.cache
+    sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    calls = p.bind_step(run.q, c["k"], c["v"], c["seqlens"], run.kpool, c["wq"], c["wk"], mode="step")
+    for t in (p.scores, p.out, p.lse):
+        t.zero_()
+    p.block_idx.fill_(-7)
+    p.n_sel.fill_(-7)
+    for call in calls:
+        call()
+    torch.cuda.synchronize()
+    assert_same_step([t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], sep, w.name)
 
 
 def test_step_replays_as_hip_graph():
@@ -217,21 +233,21 @@ def test_step_replays_as_hip_graph():
 
 
 @pytest.mark.parametrize("splits", [4, 8])
-def test_fused_step_many_workgroups(splits):
+def test_decode_step_many_workgroups(splits):
     """128 x 8 pairs at 4 and 8 splits: 4096 and 8192 workgroups, more than the compute units hold
-    at once, so a pair's splits run in different dispatch rounds before the last one merges.
-    Against the separate calls, twice in a row on one workspace."""
-    w = DecodeWorkload(name="fused_rounds", B=128, Hq=16, Hkv=8, d=64, bs=64, budget=512, seed=33,
+    at once, so a pair's splits run in different dispatch rounds.  Against the separate calls,
+    twice in a row on one workspace."""
+    w = DecodeWorkload(name="step_rounds", B=128, Hq=16, Hkv=8, d=64, bs=64, budget=512, seed=33,
                        L_range=(600, 4000))
-    run = build_and_run(w, num_splits=splits, mode="fused")
+    run = build_and_run(w, num_splits=splits, mode="step")
     p = run.plan
     assert p.num_splits == splits
     args = (run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"], run.cache["wk"])
-    fused = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    got = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
     p.step(run.q, *args, mode="calls")
     torch.cuda.synchronize()
     sep = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
-    assert_same_step(fused, sep, "first")
-    p.step(run.q, *args, mode="fused")
+    assert_same_step(got, sep, "first")
+    p.step(run.q, *args, mode="step")
     torch.cuda.synchronize()
     assert_same_step([t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], sep, "second")

@@ -4,7 +4,7 @@ A decode reads K/V rows t < seqlens[b] only.  Here the rows between each
 sequence's context end and the cache capacity hold NaN, and the capacity is
 not a multiple of the block size, so the last (b, KV head)'s tail block runs
 past the end of its rows.  Every decode entry point (the three-call step, the
-one-launch gate + select form, the fused step, the dense ground truth and the
+one-launch gate + select form, seer_decode_step, the dense ground truth and the
 per-head decode) must still match the fp64 oracle, which sees only the
 context rows ("SeerAttention-R: Sparse Attention Adaptation for Long
 Reasoning", abstract: the decoding kernel attends the kept blocks and the
@@ -73,7 +73,7 @@ def workload(case):
     return DecodeWorkload(name=name, B=B, Hq=Hq, Hkv=Hkv, d=d, bs=bs, budget=budget, seed=40 + len(name)), lens
 
 
-@pytest.mark.parametrize("mode", ["calls", "gate_select", "fused"])
+@pytest.mark.parametrize("mode", ["calls", "gate_select", "step"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_step_ignores_rows_past_the_context(case, mode):
     w, lens = workload(case)
