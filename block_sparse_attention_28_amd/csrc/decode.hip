@@ -11,8 +11,8 @@
 // The kernel bodies, and the description of their gfx950 mapping (LDS-direct
 // K/V tile loads, both products on v_mfma_f32_16x16x32_bf16 with the group's
 // query heads as the N dimension, log2-domain online softmax, per-split
-// (o, m, l) partials), are in decode_items.hpp, shared with the two-launch
-// decode step.  This file holds the launches: the split kernel, the log-sum-exp merge
+// (o, m, l) partials), are in decode_items.hpp, shared with the decode step
+// (step.hip).  This file holds the launches: the split kernel, the log-sum-exp merge
 // of the splits, and the dense ground-truth form with its block masses.
 #include "decode_items.hpp"
 

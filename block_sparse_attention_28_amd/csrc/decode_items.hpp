@@ -1,8 +1,8 @@
 // decode_items.hpp -- device bodies of the sparse-decode split and its merge.
 //
 // Used by the standalone kernels (decode.hip), the per-head form (heads.hip)
-// and the two-launch decode step (step.hip); the Mem policy (seer_device.hpp)
-// says how data handed to another workgroup is written and read.
+// and the decode step (step.hip); the Mem policy (seer_device.hpp) says how
+// data handed between launches is read and written.
 //
 // Operation ("SeerAttention-R: Sparse Attention Adaptation for Long
 // Reasoning", abstract): a decoding kernel that reads only the KV blocks the
@@ -35,8 +35,7 @@
 // At the end each wave's heads and then the 4 waves are combined, and the
 // split writes (unnormalised o, running max, running sum) per head -- or,
 // with a single split, the final normalised output directly.  A merge of the
-// splits by log-sum-exp follows (a second kernel, or the pair's last split in
-// the two-launch step).
+// splits by log-sum-exp follows in a second kernel.
 #pragma once
 
 #include "seer_device.hpp"

@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_
     constexpr int PH = 64 / CH;           // row phases per wave (4)
     constexpr int RPL = kPBS / PH;        // rows per lane and item (16)
     static_assert(D == 128, "one wave covers a 256-byte row in 16 lanes");
+    static_assert(PB == 16, "the projection's MFMA columns are the chunk's 16 blocks");
     const int blk0 = blockIdx.x * PB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     // wave-uniform, so that the Q / K descriptor choice per item stays scalar
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_
     }
     __syncthreads();
     // A[p][r] = Wq[h][r] . qbar_p ; C[p][r] = Wk[h][r] . kbar_p ; zero for dg <= r < dgp.
-    // v_mfma_f32_16x16x4f32 with W rows as M (16-row tiles), the PB pooled blocks
-    // as N (columns PB..15 zero) and the D terms split into four contiguous
+    // v_mfma_f32_16x16x4f32 with W rows as M (16-row tiles), the chunk's pooled
+    // blocks as N (columns nblk..15 zero) and the D terms split into four contiguous
     // quarters, one per k slot (slot kq carries term kq D/4 + s at step s).  Wave
     // w projects tensor w & 1, row tiles (w >> 1) + 2 m.
     constexpr int QK = D / 4;

@@ -135,7 +135,8 @@ __device__ __forceinline__ float4 as_float4(uint4 u) {
     return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
 }
 
-// Producer and consumer in different launches on one stream.
+// How the kernel bodies read and write data that another launch produced or
+// consumes (launches on one stream): plain loads and stores.
 struct LaunchMem {
     __device__ static int ldi(const int32_t *p) { return *p; }
     __device__ static float ldf(const float *p) { return *p; }
@@ -143,29 +144,6 @@ struct LaunchMem {
     __device__ static void sti(int32_t *p, int v) { *p = v; }
     __device__ static void stf(float *p, float v) { *p = v; }
     __device__ static void stf2(float2 *p, float x, float y) { *p = make_float2(x, y); }
-};
-
-// Producer and consumer in one launch, possibly on different XCDs (each with
-// its own L2): device-coherent loads and stores (sc1), which neither hit a
-// stale L2 line nor leave data behind in one.
-struct DeviceMem {
-    __device__ static int ldi(const int32_t *p) {
-        return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __device__ static float ldf(const float *p) {
-        return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __device__ static float2 ldf2(const float2 *p) {
-        const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float2 *>(p)), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-    }
-    __device__ static void sti(int32_t *p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-    __device__ static void stf(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-    __device__ static void stf2(float2 *p, float x, float y) {
-        const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
-        __hip_atomic_store(reinterpret_cast<uint64_t *>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 };
 
 }  // namespace seer
