@@ -115,6 +115,23 @@ MUTATIONS = [
      T_pipe.test_prefill_gate_single_entry_projections_closed_form),
     ("a kept block's last token left out", "for (int t = idx[i] * bs; t < (idx[i] + 1) * bs; ++t)",
      "for (int t = idx[i] * bs; t < (idx[i] + 1) * bs - 1; ++t)", lambda: T_att.test_sparse_equals_masked_dense(0)),
+    ("decode output weighs the keys instead of the values",
+     "oh[c] += wt * so_bf16_to_f64(v[(int64_t)t * kv_row_stride + c]);",
+     "oh[c] += wt * so_bf16_to_f64(k[(int64_t)t * kv_row_stride + c]);",
+     lambda: T_att.test_sparse_equals_masked_dense(0)),
+    ("prefill softmax scale dropped",
+     "            z[tt] = scale * dot;\n            if (z[tt] > m)\n                m = z[tt];\n        }\n        double *ot",
+     "            z[tt] = dot;\n            if (z[tt] > m)\n                m = z[tt];\n        }\n        double *ot",
+     lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
+    ("prefill output weighs the keys instead of the values",
+     "ot[c] += wt * so_bf16_to_f64(v[(int64_t)tt * row_stride + c]);",
+     "ot[c] += wt * so_bf16_to_f64(k[(int64_t)tt * row_stride + c]);",
+     lambda: T_pipe.test_prefill_keep_all_is_causal_attention(512, 64)),
+    ("prefill lse in log2 units", "lse[t - t_lo] = m + log(denom);", "lse[t - t_lo] = m + log2(denom);",
+     T_pipe.test_prefill_attention_equals_masked_dense),
+    ("prefill block mass not divided by the row's softmax sum",
+     "row[tt / bs] += exp(z[tt] - m) / denom / (t1 - t0);", "row[tt / bs] += exp(z[tt] - m) / (t1 - t0);",
+     lambda: T_gt.test_prefill_mass_equals_torch_causal_softmax(256, 64)),
 ]
 
 
