@@ -164,14 +164,15 @@ __global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_
 // The k largest of the n keys of one row in LDS (0 < k < n), ids ascending to
 // out, by one wave: the same rule and steps as wave_topk_from_keys (8-bit radix
 // passes from the top digit over a 256-bin LDS histogram, then one sweep in id
-// order), with the first 64 KR keys held in registers through all passes, so a
-// pass issues its histogram atomics back to back instead of after a key read each.
+// order, stopping once the digits so far single out a bin taken whole), with the
+// first 64 KR keys held in registers through all passes, so a pass issues its
+// histogram atomics back to back instead of after a key read each.
 template <int KR>
 __device__ __forceinline__ void wave_topk_row(int n, int k, const uint32_t *keys, int *hist, int32_t *out, int lane) {
     uint32_t kreg[KR];
 #pragma unroll
     for (int r = 0; r < KR; ++r) kreg[r] = lane + 64 * r < n ? keys[lane + 64 * r] : 0u;
-    uint32_t prefix = 0;
+    uint32_t prefix = 0, mask = 0xFFFFFFFFu;  // the digits found so far, and the bits they cover
     int need = k;  // keys still to take among those matching `prefix`
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
@@ -195,12 +196,13 @@ __device__ __forceinline__ void wave_topk_row(int n, int k, const uint32_t *keys
         const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
         const int incl = wave_inclusive_scan(local, lane);
         const int excl = incl - local;
-        int digit = 0, rest = 0, cum = excl;
+        int digit = 0, rest = 0, whole = 0, cum = excl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (cum < need && cum + cnt[i] >= need) {  // the digit where the count reaches need
                 digit = 255 - 4 * lane - i;
                 rest = need - cum;
+                whole = rest == cnt[i];
             }
             cum += cnt[i];
         }
@@ -209,8 +211,12 @@ __device__ __forceinline__ void wave_topk_row(int n, int k, const uint32_t *keys
         prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, src) << shift;
         need = __builtin_amdgcn_readlane(rest, src);
         wave_lds_sync();  // every lane has read the bins before the next pass clears them
+        if (__builtin_amdgcn_readlane(whole, src)) {  // a bin taken whole: no further digit matters
+            mask = 0xFFFFFFFFu << shift;
+            break;
+        }
     }
-    // keep keys > T and the first `need` keys == T, in id order
+    // keep keys > T and the first `need` keys == T, in id order, on the bits of `mask`
     const uint32_t T = prefix;
     int written = 0, eq_seen = 0;
     for (int base = 0, r = 0; base < n; base += 64, ++r) {
@@ -220,6 +226,7 @@ __device__ __forceinline__ void wave_topk_row(int n, int k, const uint32_t *keys
         for (int rr = 0; rr < KR; ++rr)
             if (r == rr) key = kreg[rr];
         if (r >= KR) key = j < n ? keys[j] : 0u;
+        key &= mask;
         const bool eq = j < n && key == T;
         const uint64_t eq_mask = __ballot(eq);
         const bool take = j < n && (key > T || (eq && eq_seen + lanes_below(eq_mask) < need));

@@ -9,7 +9,9 @@
 //     largest key T and how many keys equal to T to take.  Every wave scans
 //     the 256-bin histogram itself, so a pass costs one barrier; histograms
 //     rotate over three buffers, and the one cleared during a pass was last
-//     read two passes before;
+//     read two passes before.  The passes stop once the digits so far single
+//     out a bin that is taken whole: every key in it is kept, so the keys
+//     compare on those digits only, and the kept set is the same;
 //   * one sweep in id order places each kept id: its position is the number
 //     of kept ids below it, from per-wave ballot counts.
 #pragma once
@@ -95,7 +97,7 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
         const int j = tid + i * NT;
         kreg[i] = j < nc ? keys[j] : 0u;
     }
-    uint32_t prefix = 0;
+    uint32_t prefix = 0, mask = 0xFFFFFFFFu;  // the digits found so far, and the bits they cover
     int need = k;  // keys still to take among those matching `prefix` so far
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
@@ -118,7 +120,7 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
         const int local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
         const int incl = wave_inclusive_scan(local, lane);
         const int excl = incl - local;
-        int digit = 0, rest = 0;
+        int digit = 0, rest = 0, whole = 0;
         {
             int cum = excl;
 #pragma unroll
@@ -126,6 +128,7 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
                 if (cum < need && cum + cnt[i] >= need) {  // the one digit where the count crosses need
                     digit = 255 - 4 * lane - i;
                     rest = need - cum;
+                    whole = rest == cnt[i];
                 }
                 cum += cnt[i];
             }
@@ -134,8 +137,14 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
         const int src = hit ? (int)__builtin_ctzll(hit) : 0;
         prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, src) << shift;
         need = __builtin_amdgcn_readlane(rest, src);
+        if (__builtin_amdgcn_readlane(whole, src)) {  // the bin is taken whole: no further digit matters
+            mask = 0xFFFFFFFFu << shift;
+            break;
+        }
     }
-    // Keep keys > T and the first `need` keys == T in id order.
+    // Keep keys > T and the first `need` keys == T in id order (on the bits of
+    // `mask`: with a bin taken whole, every key of the bin counts as equal to T
+    // and `need` is its size).
     const uint32_t T = prefix;
     int gt_seen = 0, eq_seen = 0;
     for (int base = 0, round = 0, i = 0; base < nc; base += NT, round ^= 1, ++i) {
@@ -145,7 +154,7 @@ __device__ __forceinline__ int block_select_keys(const uint32_t *keys, int nc, c
         for (int r = 0; r < KR; ++r)
             if (i == r) key = kreg[r];
         if (i >= KR) key = j < nc ? keys[j] : 0u;
-        const bool gt = j < nc && key > T, eq = j < nc && key == T;
+        const bool gt = j < nc && (key & mask) > T, eq = j < nc && (key & mask) == T;
         const uint64_t gt_mask = __ballot(gt), eq_mask = __ballot(eq);
         if (lane == 0) {
             sm.wcnt[round][0][wave] = __popcll(gt_mask);

@@ -87,12 +87,13 @@ __device__ __forceinline__ void wave_load_keys(const float *scores, int n, uint3
 }
 
 // Select the k largest of the n keys in LDS (0 < k < n), write their ids
-// ascending to out[0..k) through Mem.  hist: LDS scratch of 256 words private
+// ascending to out[0..k) through Mem.  8-bit radix passes from the top digit,
+// stopping once the digits so far single out a bin that is taken whole.  hist: LDS scratch of 256 words private
 // to this wave.  Every lane of the wave must call it.
 template <class Mem>
 __device__ __forceinline__ void wave_topk_from_keys(int n, int k, uint32_t *keys, int *hist, int32_t *out,
                                                     int lane) {
-    uint32_t prefix = 0;
+    uint32_t prefix = 0, mask = 0xFFFFFFFFu;  // the digits found so far, and the bits they cover
     int need = k;  // keys still to take among those matching `prefix` so far
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
@@ -116,7 +117,7 @@ __device__ __forceinline__ void wave_topk_from_keys(int n, int k, uint32_t *keys
         const uint64_t hit = __ballot(excl < need && incl >= need);
         int src = __ffsll((long long)hit) - 1;
         src = src < 0 ? 0 : src;
-        int digit = 0, rest = 0;
+        int digit = 0, rest = 0, whole = 0;
         if (lane == src) {
             int cum = excl;
 #pragma unroll
@@ -124,6 +125,7 @@ __device__ __forceinline__ void wave_topk_from_keys(int n, int k, uint32_t *keys
                 if (cum + cnt[i] >= need) {
                     digit = 255 - 4 * lane - i;
                     rest = need - cum;
+                    whole = rest == cnt[i];
                     break;
                 }
                 cum += cnt[i];
@@ -133,12 +135,18 @@ __device__ __forceinline__ void wave_topk_from_keys(int n, int k, uint32_t *keys
         need = __builtin_amdgcn_readlane(rest, src);
         prefix |= (uint32_t)digit << shift;
         wave_lds_sync();
+        // A bin taken whole: every key in it is kept, so no further digit matters.
+        if (__builtin_amdgcn_readlane(whole, src)) {
+            mask = 0xFFFFFFFFu << shift;
+            break;
+        }
     }
+    // Keep keys > T and the first `need` keys == T in id order, on the bits of `mask`.
     const uint32_t T = prefix;
     int written = 0, eq_seen = 0;
     for (int base = 0; base < n; base += 64) {
         const int j = base + lane;
-        const uint32_t key = j < n ? keys[j] : 0u;
+        const uint32_t key = j < n ? keys[j] & mask : 0u;
         const bool eq = j < n && key == T;
         const uint64_t eq_mask = __ballot(eq);
         const bool take = j < n && (key > T || (eq && eq_seen + lanes_below(eq_mask) < need));
