@@ -93,8 +93,10 @@ __global__ __launch_bounds__(256) void prefill_pool_project_kernel(const uint16_
         {  // the whole offset in the per-lane part, which is what the range check covers
             const uint32_t voff = (uint32_t)(blk0 + (it >> 1)) * kPBS * D * 2u + lane_off;
             const __amdgpu_buffer_rsrc_t r = (it & 1) ? rk : rq;
+            // each row is read once here: streaming loads keep the pass from
+            // evicting what the score and attention kernels reuse
 #pragma unroll
-            for (int m = 0; m < RPL; ++m) cur[m] = buf_ld16(r, voff + (uint32_t)(m * PH * D * 2), 0);
+            for (int m = 0; m < RPL; ++m) cur[m] = buf_ld16_nt(r, voff + (uint32_t)(m * PH * D * 2), 0);
         }
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
