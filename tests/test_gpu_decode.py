@@ -232,6 +232,24 @@ def test_step_replays_as_hip_graph():
             assert torch.equal(a, b), f"replay {step} differs from the eager step"
 
 
+def test_decode_step_widest_pooled_table():
+    """The step at the widest pooled table it accepts (16128 blocks of 64 tokens, about a million
+    tokens) with groups of 8 and d 128, where the selection keys and the decode tiles take the most
+    LDS: against the oracle, and bit for bit against the separate calls."""
+    w = DecodeWorkload(name="step_wide_table", B=1, Hq=8, Hkv=1, d=128, bs=64, budget=700 * 64, seed=34,
+                       L=16128 * 64)
+    run = build_and_run(w, mode="step")
+    assert run.nb_max == 16128
+    st = check_sequence(run, 0, oracle_sequence(run, 0))
+    say(f"[gpu] step_wide_table max_err={st['max_err']:.2e} excused={st['excused']}")
+    p = run.plan
+    got = [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)]
+    p.step(run.q, run.cache["k"], run.cache["v"], run.cache["seqlens"], run.kpool, run.cache["wq"],
+           run.cache["wk"], mode="calls")
+    torch.cuda.synchronize()
+    assert_same_step(got, [t.clone() for t in (p.scores, p.block_idx, p.n_sel, p.out, p.lse)], w.name)
+
+
 @pytest.mark.parametrize("splits", [4, 8])
 def test_decode_step_many_workgroups(splits):
     """128 x 8 pairs at 4 and 8 splits: 4096 and 8192 workgroups, more than the compute units hold
