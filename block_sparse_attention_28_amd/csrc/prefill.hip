@@ -529,9 +529,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     };
     auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's loads are in LDS
     // S^T of this wave's 32 keys and 32 query rows: s[4 a + b] holds key
-    // 32 kh + 8 a + 4 hl + b of query row qtok.  The even and odd k-steps
-    // accumulate separately (two independent MFMA chains instead of one chain
-    // of 8) and are added at the end.
+    // 32 kh + 8 a + 4 hl + b of query row qtok.  One accumulation chain over
+    // the 8 k-steps: the P V products of the previous block fill the gaps
+    // between its dependent MFMAs, and no VALU adds of partial sums remain.
     // kread: the K operand of this wave's 32 keys for every k-step (offsets masked
     // to the buffer's 16 KiB, which they never exceed: the compiler then sees that
     // the reads cannot touch a buffer being loaded).  smma: the MFMAs.
@@ -543,18 +543,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                 kb + ((krow_off + (((2 * ks + hl) ^ (n & 15)) << 4)) & (KBYTES - 1)));
     };
     auto smma = [&](f32x16_t &s, const bf16x8_t (&ka)[KS]) {
-        f32x16_t s1;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s[e] = 0.f;
-            s1[e] = 0.f;
-        }
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ks += 2) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], s, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks + 1], qop[ks + 1], s1, 0, 0, 0);
-        }
-        s += s1;
+        for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], s, 0, 0, 0);
     };
     auto scores = [&](f32x16_t &s, const char *kb) {
         bf16x8_t ka[KS];
