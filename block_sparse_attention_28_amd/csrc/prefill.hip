@@ -510,8 +510,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         j = j < 0 ? 0 : (j > i ? i : j);
         return j * kPBS;
     };
-    auto dma = [&](int it, char *dst, __amdgpu_buffer_rsrc_t rs, const uint32_t (&dv)[DMA_PER_WAVE]) {
-        const int k0 = block_start(it);
+    auto dma_at = [&](int k0, char *dst, __amdgpu_buffer_rsrc_t rs, const uint32_t (&dv)[DMA_PER_WAVE]) {
         char *base = dst + wave * (DMA_PER_WAVE * 1024);
         if (k0 + kPBS <= L) {  // a whole block: the row offset is scalar
 #pragma unroll
@@ -526,6 +525,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
                                                          16, (int)dv[qd] - (over > 0 ? over : 0) * D * 2, k0 * D * 2, 0, 0);
             }
         }
+    };
+    auto dma = [&](int it, char *dst, __amdgpu_buffer_rsrc_t rs, const uint32_t (&dv)[DMA_PER_WAVE]) {
+        dma_at(block_start(it), dst, rs, dv);
     };
     auto loads_done = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0): this wave's loads are in LDS
     // S^T of this wave's 32 keys and 32 query rows: s[4 a + b] holds key
@@ -554,12 +556,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         smma(s, ka);
     };
     // Causal / length masks: only the diagonal block and a partial last block need them.
-    auto is_edge = [&](int it) {
-        const int k0 = block_start(it);
-        return k0 == i * kPBS || k0 + kPBS > L;
-    };
-    auto mask = [&](f32x16_t &s, int it) {
-        const int k0 = block_start(it);
+    auto edge_at = [&](int k0) { return k0 == i * kPBS || k0 + kPBS > L; };
+    auto mask_at = [&](f32x16_t &s, int k0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int ktok = k0 + 32 * kh + 8 * (e >> 2) + 4 * hl + (e & 3);
@@ -647,16 +645,22 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
     // its maximum.  At its start it issues the loads of K of block it + 2 and V
     // of block it + 1 into the buffers the last iteration finished with; they
     // land while it computes.  One barrier per iteration.  Buffer parity follows
-    // it, so the loop is unrolled by two.
+    // it, so the loop is unrolled by two.  The first tokens of blocks it + 1 and
+    // it + 2 are carried from iteration to iteration, so each reads one block id
+    // (block it + 3's) and before it is needed.
     f32x16_t sA, sB;
+    int kn1 = 0, kn2 = 0;
     if (cnt > 0) {
-        dma(0, kbuf0, krs, kdv);
-        dma(0, vbuf0, vrs, vdv);
-        if (cnt > 1) dma(1, kbuf1, krs, kdv);
+        const int k0 = block_start(0);
+        kn1 = cnt > 1 ? block_start(1) : 0;
+        kn2 = cnt > 2 ? block_start(2) : 0;
+        dma_at(k0, kbuf0, krs, kdv);
+        dma_at(k0, vbuf0, vrs, vdv);
+        if (cnt > 1) dma_at(kn1, kbuf1, krs, kdv);
         loads_done();
         __syncthreads();
         scores(sA, kbuf0);
-        if (is_edge(0)) mask(sA, 0);
+        if (edge_at(k0)) mask_at(sA, k0);
         prep(sA, true);
         __syncthreads();  // block 0's K buffer is free
     }
@@ -667,16 +671,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(const uint16_
         char *const k_this = P ? kbuf1 : kbuf0, *const k_next = P ? kbuf0 : kbuf1;
         char *const v_this = P ? vbuf1 : vbuf0, *const v_next = P ? vbuf0 : vbuf1;
         const bool has_next = it + 1 < cnt;
-        if (it + 2 < cnt) dma(it + 2, k_this, krs, kdv);  // where block it's K was
-        if (has_next) dma(it + 1, v_next, vrs, vdv);       // where block it - 1's V was
+        if (it + 2 < cnt) dma_at(kn2, k_this, krs, kdv);  // where block it's K was
+        if (has_next) dma_at(kn1, v_next, vrs, vdv);       // where block it - 1's V was
+        const int k1 = kn1;
+        const int kn3 = it + 3 < cnt ? block_start(it + 3) : 0;
         // One straight-line region (no branch inside) so that the MFMAs of the
         // scores and of P V interleave with the VALU work on the weights.
         bf16x8_t pb[2];
         scores(s_next, k_next);  // on the last step this reads a stale buffer: unused
         weights(s_cur, pb);
         pv(pb, v_this);
-        if (has_next && is_edge(it + 1)) mask(s_next, it + 1);
+        if (has_next && edge_at(k1)) mask_at(s_next, k1);
         prep(s_next, has_next);
+        kn1 = kn2;
+        kn2 = kn3;
         loads_done();
         __syncthreads();  // loads visible; reads of this iteration's buffers done
     };
