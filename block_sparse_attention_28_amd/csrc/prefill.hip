@@ -18,8 +18,10 @@
 //                          keys; one wave per row then selects the exact
 //                          top-(k_i - 1) of j < i with lower-id ties, then the
 //                          diagonal (nb up to 2048)
-//   prefill_gate_scores  : beyond 2048 blocks, S through the workspace in fp32
-//   prefill_select_rows    64x64 LDS tiles, and one wave per row selecting
+//   prefill_gate_scores  : beyond 2048 blocks, S into the workspace in fp32
+//                          (64x64 tiles through LDS)
+//   prefill_select_rows  : beyond 2048 blocks, one wave per row selecting from
+//                          the workspace scores by the same rule
 //   prefill_attention    : 64 query rows per workgroup; each wave takes 32
 //                          rows and one 32-key half of every kept block, MFMA
 //                          v_mfma_f32_32x32x16_bf16.  S^T = K Q^T so that each
