@@ -41,7 +41,7 @@ METRIC = "sparse-decode effective KV GB/s (% of HBM peak) + us/step at 90% spars
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DECODE_L64K_S90.name, choices=sorted(DECODE_WORKLOADS))
     ap.add_argument("--layers", type=int, default=8, help="distinct KV caches rotated across steps")
