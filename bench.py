@@ -622,9 +622,10 @@ def bench_prefill(steps, dev, ceil=None):
                 torch.cuda.synchronize()
                 got[given].append(e0.elapsed_time(e1) * 1e3)
         med = lambda v: sorted(v)[len(v) // 2]
-        return med(got[False]), med(got[True])
+        # the gate's share: the median of the differences of adjacent calls
+        return med(got[False]), med(got[True]), med([a - b for a, b in zip(got[False], got[True])])
 
-    us_total, us_attn = timed_pair()
+    us_total, us_attn, us_gate = timed_pair()
     # ground truth: dense causal attention plus every (query block, key block) mass
     mass = torch.empty((pw.B, pw.H, nb, nb), dtype=torch.float32, device=dev)
     gt = seer.seer_prefill_block_mass(x["q"], x["k"], x["v"], pw.bs, ss, out, mass, lse, bind=True)
@@ -642,7 +643,7 @@ def bench_prefill(steps, dev, ceil=None):
     flops = prefill_flops(counts, pw.bs, pw.d)
     tflops = flops / (us_attn * 1e-6) / 1e12
     return {"workload": pw.name, "steps": steps, "us_per_prefill": round(us_total, 1),
-            "us_gate": round(us_total - us_attn, 1), "us_attention": round(us_attn, 1),
+            "us_gate": round(us_gate, 1), "us_attention": round(us_attn, 1),
             "kept_blocks_per_head": int(counts[0, 0].sum()), "algorithmic_gflop": round(flops / 1e9, 1),
             "ground_truth": {"call": "seer_prefill_block_mass", "us": round(us_gt, 1),
                              "dense_attention_gflop": round(pw.B * pw.H * dense_flops / 1e9, 1),
