@@ -38,3 +38,14 @@ def test_traffic_records_are_well_formed(record):
         rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"], abs=2)
     for f in rec["sources"]:
         assert os.path.exists(os.path.join(ROOT, f)), f
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    """The benchmark measures one GPU: --gpus above 1 exits with status 2 and says so."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
