@@ -27,9 +27,15 @@ __global__ __launch_bounds__(256) void pool_k_kernel(const uint16_t *k, int64_t 
     const int c = tid % CH, rg = tid / CH;
     const uint16_t *base = k + b * sk_b + h * sk_h + (int64_t)j * BS * sk_t + c * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // Streaming loads: a block is pooled once, and caching it would only push
+    // out lines that other work reuses.
     uint4 rows[BS / RG];
 #pragma unroll
-    for (int i = 0; i < BS / RG; ++i) rows[i] = *reinterpret_cast<const uint4 *>(base + (int64_t)(rg + i * RG) * sk_t);
+    for (int i = 0; i < BS / RG; ++i) {
+        const u32x4_t t =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + (int64_t)(rg + i * RG) * sk_t));
+        rows[i] = make_uint4(t.x, t.y, t.z, t.w);
+    }
 #pragma unroll
     for (int i = 0; i < BS / RG; ++i) {
         const uint4 w = rows[i];
